@@ -1,0 +1,190 @@
+/*
+ * moe_decode.h - C ABI of the MI355X (gfx950) quantized MoE decode library.
+ *
+ * What it computes (one MoE FFN layer, per token row t, rows independent):
+ *   u_t      = h_t / sqrt(mean(h_t^2) + eps)                 RMS normalisation, weight 1
+ *   logits   = W_r u_t                                       router GEMV
+ *   ids, w   = top-k of logits (descending, ties -> lower id);
+ *              w = softmax restricted to the k selected logits (renormalised)
+ *   a_e      = silu(W_gate,e u_t) * (W_up,e u_t)             SwiGLU, each selected expert e
+ *   a_s      = the same for the shared expert
+ *   out_t    = h_t + sum_i w_i W_down,ids_i a_ids_i + sigmoid(gvec . u_t) W_down,s a_s
+ *   h_out_t  = bf16(out_t), round to nearest even
+ * Sources: PureDrive-35B-A3B-MLX model card, "Summary" (top-8 of 256 routed
+ * experts plus one shared expert; 6-bit routed, 8-bit shared/router) and "FAQ"
+ * (every selected expert runs); flash-moe news page (ja.news.hada.io topic
+ * 27758), "FMA-optimised dequant kernel" (weight = code*scale + bias, group
+ * affine), "Metal Compute Shaders" (SwiGLU, RMS normalisation, MoE combine +
+ * residual + gate) and "Deferred GPU Expert Compute" (combine, norm and
+ * residual stay on the GPU and feed the next layer directly).
+ *
+ * Conventions for every entry point:
+ *   - return 0 (MOE_OK) on success or a negative MOE_ERR_* code; the message
+ *     of the last failure on the calling thread is moe_last_error().
+ *   - all argument validation is host code and runs before any launch; a
+ *     failed validation launches nothing and touches no buffer.
+ *   - "dev" pointers are device (HBM) addresses, "host" pointers host
+ *     addresses. The caller owns every buffer; the library never allocates
+ *     device memory and keeps no pointer beyond a call.
+ *   - launches are asynchronous on the given stream (a hipStream_t, NULL =
+ *     the default stream); device-side faults surface at the caller's next
+ *     synchronisation.
+ *   - results are bitwise deterministic, and for T <= 8 row t of a T-row
+ *     call is bitwise equal to a T = 1 call on that row alone.
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* moe_stream_t; /* a hipStream_t */
+
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,     /* null pointer, bad size, bad shape field */
+  MOE_ERR_UNSUPPORTED = -2,     /* bit width / group / dimension not supported */
+  MOE_ERR_ALIGNMENT = -3,       /* device pointer not aligned as documented */
+  MOE_ERR_WORKSPACE = -4,       /* workspace smaller than moe_workspace_bytes() */
+  MOE_ERR_HIP = -5              /* a HIP runtime call failed */
+};
+
+/* Shape of one MoE layer. Limits: hidden, inter, shared_inter multiples of 64
+ * in [64, 16384]; 1 <= top_k <= min(n_experts, 16); n_experts <= 1024;
+ * expert_bits, shared_bits in {2, 3, 4, 6, 8}; router_bits in {2, 3, 4, 6, 8}
+ * or 16 (dense bf16 router); group must be 64; rms_eps > 0. */
+typedef struct moe_shape {
+  int32_t hidden;        /* H */
+  int32_t n_experts;     /* E routed experts */
+  int32_t inter;         /* I, routed expert intermediate size */
+  int32_t top_k;         /* k */
+  int32_t shared_inter;  /* I_s, shared expert intermediate size */
+  int32_t router_bits;   /* 16 = dense bf16 [E, H]; else group-affine codes */
+  int32_t expert_bits;
+  int32_t shared_bits;
+  int32_t group;         /* 64 */
+  float rms_eps;         /* 1e-6 */
+} moe_shape_t;
+
+/*
+ * Packed quantised matrix W [rows, cols], group-affine along cols in groups of
+ * 64: W[r, c] = code[r, c] * scale[r, c/64] + bias[r, c/64] (flash-moe news
+ * page, "FMA-optimised dequant kernel"). One matrix block is
+ *   codes  : rows * row_bytes(bits, cols), row-major, rows back to back
+ *   (pad)  : to a multiple of 256 bytes
+ *   sb     : rows * (cols/64) dwords; dword = scale bf16 (bits 0-15) |
+ *            bias bf16 (bits 16-31), row-major
+ *   (pad)  : to a multiple of 256 bytes
+ * Codes inside a row (code j = column j):
+ *   bits 2, 4, 8 : dense, LSB first: code j at bit offset bits*j of the row.
+ *   bits 6       : units of 16 codes in 3 dwords. Unit u holds codes
+ *                  16u..16u+15 (local index c = 0..15). dword 0 holds the low
+ *                  4 bits of c = 0..7 at bit 4c, dword 1 those of c = 8..15 at
+ *                  bit 4(c-8); dword 2 holds the high 2 bits: for c = 8d + i +
+ *                  4s (d, s in {0,1}, i in 0..3) at bit 2(4d + i) + 16s.
+ *   bits 3       : 10 codes per dword, code j in dword j/10 at bit 3(j%10);
+ *                  bits 30-31 zero; each row padded to whole dwords with zero.
+ * row_bytes = cols*bits/8 for bits 2/4/6/8, 4*ceil(cols/10) for bits 3.
+ */
+int64_t moe_matrix_bytes(int32_t bits, int32_t rows, int32_t cols);
+
+/* Byte offsets of the parts of one layer block (each 256-byte aligned):
+ * router (packed matrix [E, H], or dense bf16 [E, H] when router_bits = 16),
+ * gate vector (bf16 [H]), shared expert, then routed expert e at
+ * expert0 + e * expert_stride. An expert is three packed matrices back to
+ * back: gate [I, H], up [I, H], down [H, I]. */
+typedef struct moe_layer_layout {
+  int64_t router;
+  int64_t gatevec;
+  int64_t shared;         /* shared expert block */
+  int64_t shared_up;      /* offsets of up / down inside an expert block */
+  int64_t shared_down;
+  int64_t expert0;
+  int64_t expert_stride;
+  int64_t expert_up;
+  int64_t expert_down;
+  int64_t total_bytes;    /* whole layer block */
+} moe_layer_layout_t;
+
+/* Validates the shape (pure host code). */
+int32_t moe_validate_shape(const moe_shape_t* shape);
+
+/* Fills *out for a valid shape. */
+int32_t moe_layer_layout(const moe_shape_t* shape, moe_layer_layout_t* out);
+
+/* Bytes of workspace a decode call with up to T rows needs (1 <= T <= 32).
+ * The same workspace serves moe_decode_layer and moe_decode_stack. Returns a
+ * negative MOE_ERR_* code for an invalid shape or T. */
+int64_t moe_workspace_bytes(const moe_shape_t* shape, int32_t T);
+
+/* Host-side packing of one matrix into the layout above.
+ * codes_host: uint8 [rows, cols], each < 2^bits; scale_host, bias_host: bf16
+ * bit patterns [rows, cols/64]; dst_host: moe_matrix_bytes() bytes, fully
+ * written (padding zero). cols must be a multiple of 64. A code >= 2^bits
+ * returns MOE_ERR_INVALID_ARG with dst partly written. */
+int32_t moe_pack_matrix(int32_t bits, int32_t rows, int32_t cols, const uint8_t* codes_host,
+                        const uint16_t* scale_host, const uint16_t* bias_host, void* dst_host);
+
+/* Inverse of moe_pack_matrix (host only). */
+int32_t moe_unpack_matrix(int32_t bits, int32_t rows, int32_t cols, const void* src_host,
+                          uint8_t* codes_host, uint16_t* scale_host, uint16_t* bias_host);
+
+/*
+ * Synthetic weights: writes the whole layer block of layer `layer` on the
+ * device (layer_dev: moe_layer_layout().total_bytes bytes, 256-byte aligned),
+ * drawing codes, bf16 scales/biases and bf16 vectors from the seeded
+ * splitmix64 counter generator (Steele, Lea & Flood, OOPSLA 2014) with
+ * per-(layer, expert) sub-seeds. The definition of the draws is the one
+ * documented with the library sources (gen kernels).
+ */
+int32_t moe_generate_layer(const moe_shape_t* shape, uint64_t seed, int32_t layer, void* layer_dev,
+                           moe_stream_t stream);
+
+/* Synthetic x rows: bf16 [T, H] ~ N(0, 1) from seed_x, written to out_dev
+ * (16-byte aligned). */
+int32_t moe_generate_rows(uint64_t seed_x, int32_t T, int32_t H, uint16_t* out_dev, moe_stream_t stream);
+
+/*
+ * One MoE layer on T rows (1 <= T <= 32).
+ *   layer_dev : layer block (layout above), 256-byte aligned
+ *   h_in_dev  : bf16 [T, H], 16-byte aligned; h_out_dev: bf16 [T, H], 16-byte
+ *               aligned, must not overlap h_in_dev
+ *   ids_dev   : int32 [T, k] selected experts (descending logit) or NULL
+ *   w_dev     : float [T, k] renormalised routing weights or NULL
+ *   ws_dev    : workspace of ws_bytes >= moe_workspace_bytes(shape, T),
+ *               256-byte aligned; contents need no initialisation.
+ * Calls that share one workspace must be ordered on one stream.
+ */
+int32_t moe_decode_layer(const moe_shape_t* shape, const void* layer_dev, int32_t T, const uint16_t* h_in_dev,
+                         uint16_t* h_out_dev, int32_t* ids_dev, float* w_dev, void* ws_dev, size_t ws_bytes,
+                         moe_stream_t stream);
+
+/*
+ * A stack of n_layers MoE layers with distinct weights: h_0 = h_in,
+ * h_{l+1} = bf16(layer_l(h_l)), h_out = h_{n_layers}. The host never waits
+ * inside the stack.
+ *   layers_host : host array of n_layers device pointers to layer blocks
+ *   ids_dev     : int32 [n_layers, T, k] or NULL; w_dev: float [n_layers, T, k] or NULL
+ *   h_trace_dev : bf16 [n_layers + 1, T, H] (h_0 .. h_L) or NULL
+ * Other arguments as for moe_decode_layer.
+ */
+int32_t moe_decode_stack(const moe_shape_t* shape, const void* const* layers_host, int32_t n_layers, int32_t T,
+                         const uint16_t* h_in_dev, uint16_t* h_out_dev, int32_t* ids_dev, float* w_dev,
+                         uint16_t* h_trace_dev, void* ws_dev, size_t ws_bytes, moe_stream_t stream);
+
+/* Message for the last failure on this thread ("" if none). Valid until the
+ * thread's next call into the library. */
+const char* moe_last_error(void);
+
+/* Library version string. */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DECODE_H */

@@ -1,0 +1,35 @@
+"""MI355X (gfx950) quantized MoE decode: C-ABI library libmoe.so + Python binding.
+
+The hot path (router GEMV, renormalised softmax top-k, group-affine dequant
+gate/up/down GEMVs with SwiGLU, sigmoid-gated shared expert, weighted combine,
+residual, layer stacking) runs entirely in the HIP kernels of libmoe.so. This
+package only marshals arguments to it; PyTorch, where used by callers, only
+provides device memory and streams.
+"""
+
+from ._lib import (  # noqa: F401
+    MOE_ERR_ALIGNMENT,
+    MOE_ERR_HIP,
+    MOE_ERR_INVALID_ARG,
+    MOE_ERR_UNSUPPORTED,
+    MOE_ERR_WORKSPACE,
+    MOE_OK,
+    MoeError,
+    header_functions,
+    lib,
+    make_shape,
+    moe_decode_layer,
+    moe_decode_stack,
+    moe_generate_layer,
+    moe_generate_rows,
+    moe_last_error,
+    moe_layer_layout,
+    moe_matrix_bytes,
+    moe_pack_matrix,
+    moe_shape_t,
+    moe_unpack_matrix,
+    moe_validate_shape,
+    moe_version,
+    moe_workspace_bytes,
+)
+from .workloads import WORKLOADS, Workload  # noqa: F401

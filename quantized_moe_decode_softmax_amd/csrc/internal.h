@@ -1,0 +1,68 @@
+// Internal declarations shared by the host code and the HIP sources of the
+// library. Not part of the public ABI (include/moe_decode.h is).
+#pragma once
+
+#include <stdint.h>
+#include <stddef.h>
+
+#include "moe_decode.h"
+
+// Layout arithmetic is used by host code (g++) and by kernels (hipcc).
+#ifdef __HIPCC__
+#define MOE_HD __host__ __device__
+#else
+#define MOE_HD
+#endif
+
+namespace moe {
+
+constexpr int kGroup = 64;
+constexpr int kMaxT = 32;
+constexpr int kMaxTopK = 16;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxDim = 16384;
+constexpr int64_t kAlign = 256;
+
+MOE_HD inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// bytes of one row of codes
+MOE_HD inline int64_t row_bytes(int bits, int cols) {
+  if (bits == 3) return 4 * (((int64_t)cols + 9) / 10);
+  return (int64_t)cols * bits / 8;
+}
+MOE_HD inline bool bits_ok(int bits) { return bits == 2 || bits == 3 || bits == 4 || bits == 6 || bits == 8; }
+
+// offsets inside one packed matrix block
+MOE_HD inline int64_t matrix_codes_bytes(int bits, int rows, int cols) { return align_up(row_bytes(bits, cols) * rows, kAlign); }
+MOE_HD inline int64_t matrix_sb_bytes(int rows, int cols) { return align_up((int64_t)rows * (cols / kGroup) * 4, kAlign); }
+MOE_HD inline int64_t matrix_bytes(int bits, int rows, int cols) {
+  return matrix_codes_bytes(bits, rows, cols) + matrix_sb_bytes(rows, cols);
+}
+
+// Workspace map (all offsets 256-aligned). T rows, up to U = min(T*k, E)
+// unique routed experts per call.
+struct WsMap {
+  int64_t raw_logits;   // float [T][E]  router dot products with h (before the RMS factor)
+  int64_t rinv;         // float [T]     1/sqrt(mean(h^2)+eps)
+  int64_t sgate;        // float [T]     sigmoid gate of the shared expert
+  int64_t ids;          // int32 [T][k]
+  int64_t wts;          // float [T][k]
+  int64_t units;        // int32 [1 + U] count, then expert ids of the unique units (ascending)
+  int64_t masks;        // uint32 [U]   rows using each unit
+  int64_t a_hi;         // bf16  [T][k+1][Imax]  SwiGLU activations, high part
+  int64_t a_lo;         // bf16  [T][k+1][Imax]  low part: a = hi + lo to 16 significant bits
+  int64_t dsum;         // float [T][k][H] routed down projections per (row, rank)
+  int64_t hbuf;         // bf16  [2][T][H] ping-pong for stacks
+  int64_t total;
+};
+
+WsMap ws_map(const moe_shape_t& s, int T);
+
+// thread-local error reporting
+int32_t set_error(int32_t code, const char* fmt, ...);
+void clear_error();
+
+int32_t check_shape(const moe_shape_t* s);
+void layout_of(const moe_shape_t& s, moe_layer_layout_t* out);
+
+}  // namespace moe

@@ -1,0 +1,77 @@
+"""Device-memory helper around the C ABI: PyTorch allocates, libmoe computes.
+
+``DeviceStack`` owns one HBM buffer per layer (filled by the library's seeded
+generator, or by the caller with packed weights), a workspace, and calls
+``moe_decode_layer`` / ``moe_decode_stack`` on the current torch stream. No
+step of the method runs here.
+"""
+
+from __future__ import annotations
+
+from typing import List, Optional, Sequence
+
+import torch
+
+from . import _lib as L
+from .workloads import Workload
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+class DeviceStack:
+    def __init__(self, shape_kwargs: dict, n_layers: int, t_max: int = 1, seed: Optional[int] = 0,
+                 device: str = "cuda:0"):
+        if not torch.cuda.is_available():
+            raise RuntimeError("DeviceStack needs a GPU (no CPU fallback exists)")
+        self.kw = dict(shape_kwargs)
+        self.shape = L.make_shape(**self.kw)
+        L.moe_validate_shape(self.shape)
+        self.layout = L.moe_layer_layout(self.shape)
+        self.n_layers, self.t_max, self.device = n_layers, t_max, device
+        self.H, self.k = self.kw["hidden"], self.kw["top_k"]
+        self.layers: List[torch.Tensor] = [
+            torch.empty(self.layout["total_bytes"], dtype=torch.uint8, device=device) for _ in range(n_layers)
+        ]
+        self.ws_bytes = L.moe_workspace_bytes(self.shape, t_max)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        if seed is not None:
+            for i, buf in enumerate(self.layers):
+                L.moe_generate_layer(self.shape, seed, i, buf.data_ptr(), _stream())
+
+    @classmethod
+    def from_workload(cls, w: Workload, n_layers: Optional[int] = None, t_max: Optional[int] = None, seed: int = 0):
+        return cls(w.shape_kwargs(), n_layers or w.n_layers, t_max or w.T, seed)
+
+    def rows(self, seed_x: int, T: int) -> torch.Tensor:
+        x = torch.empty((T, self.H), dtype=torch.bfloat16, device=self.device)
+        L.moe_generate_rows(seed_x, T, self.H, x.data_ptr(), _stream())
+        return x
+
+    def layer(self, h: torch.Tensor, l: int = 0, out: Optional[torch.Tensor] = None):
+        T = h.shape[0]
+        out = torch.empty_like(h) if out is None else out
+        ids = torch.empty((T, self.k), dtype=torch.int32, device=self.device)
+        w = torch.empty((T, self.k), dtype=torch.float32, device=self.device)
+        L.moe_decode_layer(self.shape, self.layers[l].data_ptr(), T, h.data_ptr(), out.data_ptr(), ids.data_ptr(),
+                           w.data_ptr(), self.ws.data_ptr(), self.ws_bytes, _stream())
+        return out, ids, w
+
+    def stack(self, h: torch.Tensor, n_layers: Optional[int] = None, trace: bool = False, routing: bool = True,
+              out: Optional[torch.Tensor] = None, bufs: Optional[Sequence[torch.Tensor]] = None):
+        T = h.shape[0]
+        n = n_layers or self.n_layers
+        out = torch.empty_like(h) if out is None else out
+        ids = torch.empty((n, T, self.k), dtype=torch.int32, device=self.device) if routing else None
+        w = torch.empty((n, T, self.k), dtype=torch.float32, device=self.device) if routing else None
+        tr = torch.empty((n + 1, T, self.H), dtype=torch.bfloat16, device=self.device) if trace else None
+        L.moe_decode_stack(self.shape, [b.data_ptr() for b in self.layers[:n]], T, h.data_ptr(), out.data_ptr(),
+                           None if ids is None else ids.data_ptr(), None if w is None else w.data_ptr(),
+                           None if tr is None else tr.data_ptr(), self.ws.data_ptr(), self.ws_bytes, _stream())
+        return out, ids, w, tr
+
+
+def bf16_bits(t: torch.Tensor):
+    """bf16 tensor -> numpy uint16 bit patterns (host copy)."""
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view("uint16")

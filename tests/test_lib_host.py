@@ -1,0 +1,191 @@
+"""Host-side tests of libmoe.so (no GPU needed: only host entry points are called).
+
+* the library loads and exports every function include/moe_decode.h declares;
+* shape/argument validation returns the documented error codes before any
+  launch (decode calls with bad arguments never reach the device);
+* layout sizes match the closed form, including the flash-moe news page's
+  "about 6.75 MB per expert" for the 397B shape at 4 bits ("SSD Expert
+  Streaming": 4 active experts of ~6.75 MB each), read as 6.75 MiB;
+* the packer agrees with an independent reader of the documented layout.
+"""
+
+import numpy as np
+import pytest
+
+import quantized_moe_decode_softmax_amd as moe
+from quantized_moe_decode_softmax_amd import WORKLOADS
+from tests import layout_ref
+
+
+def shape_of(name, **over):
+    kw = WORKLOADS[name].shape_kwargs()
+    kw.update(over)
+    return moe.make_shape(**kw)
+
+
+def test_library_exports_every_declared_function():
+    L = moe.lib()
+    names = moe.header_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert moe.moe_version().startswith("moe-decode")
+
+
+def test_expert_size_closed_form_matches_page():
+    # 3 matrices of 4096 x 1024 at 4 bits + a bf16 scale and bias per 64 weights
+    kw = dict(hidden=4096, n_experts=512, inter=1024, top_k=10, shared_inter=1024, router_bits=8, expert_bits=4,
+              shared_bits=4)
+    lay = moe.moe_layer_layout(moe.make_shape(**kw))
+    assert lay["expert_stride"] == 3 * 4096 * 1024 * 4 // 8 + 3 * 4096 * 1024 // 64 * 4 == 7077888
+    assert lay["expert_stride"] / 2**20 == 6.75
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_layout_matches_independent_reading(name):
+    w = WORKLOADS[name]
+    lay = moe.moe_layer_layout(moe.make_shape(**w.shape_kwargs()))
+    ref = layout_ref.layer_offsets(**w.shape_kwargs())
+    assert lay == ref
+    for k, v in lay.items():
+        assert v % 256 == 0, k
+
+
+def test_workload_sizes():
+    # 35B-A3B shape: 40 layers resident, well under the ~28 GB the model card gives for the whole model
+    lay = moe.moe_layer_layout(shape_of("a3b"))
+    assert lay["expert_stride"] == 2555904
+    total = 40 * lay["total_bytes"]
+    assert 26.0e9 < total < 28.0e9
+    # 397B shape: 60 layers fit in one 288 GB device
+    lay = moe.moe_layer_layout(shape_of("a17b"))
+    assert 60 * lay["total_bytes"] < 250e9
+    # 3-bit at 10 codes per word: rows of 4096 codes take 410 words
+    lay = moe.moe_layer_layout(shape_of("a17b_lowbit"))
+    assert lay["expert_stride"] == 2 * (1024 * 1640 + 1024 * 64 * 4) + 4096 * 412 + 4096 * 16 * 4 == 5832704
+
+
+def test_workspace_bytes():
+    s = shape_of("a3b")
+    w1 = moe.moe_workspace_bytes(s, 1)
+    w8 = moe.moe_workspace_bytes(s, 8)
+    assert 0 < w1 < w8 < 64 << 20
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_workspace_bytes(s, 0)
+    assert e.value.code == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError):
+        moe.moe_workspace_bytes(s, 33)
+
+
+@pytest.mark.parametrize(
+    "field,value,code",
+    [
+        ("expert_bits", 5, moe.MOE_ERR_UNSUPPORTED),
+        ("expert_bits", 7, moe.MOE_ERR_UNSUPPORTED),
+        ("shared_bits", 1, moe.MOE_ERR_UNSUPPORTED),
+        ("router_bits", 12, moe.MOE_ERR_UNSUPPORTED),
+        ("group", 32, moe.MOE_ERR_UNSUPPORTED),
+        ("group", 128, moe.MOE_ERR_UNSUPPORTED),
+        ("hidden", 100, moe.MOE_ERR_UNSUPPORTED),
+        ("inter", 0, moe.MOE_ERR_UNSUPPORTED),
+        ("top_k", 0, moe.MOE_ERR_INVALID_ARG),
+        ("top_k", 17, moe.MOE_ERR_INVALID_ARG),
+        ("n_experts", 0, moe.MOE_ERR_INVALID_ARG),
+        ("n_experts", 2000, moe.MOE_ERR_INVALID_ARG),
+        ("rms_eps", 0.0, moe.MOE_ERR_INVALID_ARG),
+    ],
+)
+def test_shape_validation(field, value, code):
+    s = shape_of("tiny", **{field: value})
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_validate_shape(s)
+    assert e.value.code == code
+    assert moe.moe_last_error() != ""
+
+
+def test_top_k_above_experts_rejected():
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_validate_shape(shape_of("tiny", top_k=16, n_experts=8))
+    assert e.value.code == moe.MOE_ERR_INVALID_ARG
+
+
+def test_decode_argument_errors_return_before_launch():
+    """Every one of these fails in host validation; no device pointer is touched."""
+    s = shape_of("tiny")
+    ws = moe.moe_workspace_bytes(s, 2)
+    A = 1 << 20  # 256-aligned fake addresses, never dereferenced
+    cases = [
+        (dict(T=0), moe.MOE_ERR_INVALID_ARG),
+        (dict(T=33), moe.MOE_ERR_INVALID_ARG),
+        (dict(h_in=0), moe.MOE_ERR_INVALID_ARG),
+        (dict(layer=0), moe.MOE_ERR_INVALID_ARG),
+        (dict(ws=0), moe.MOE_ERR_INVALID_ARG),
+        (dict(layer=A + 8), moe.MOE_ERR_ALIGNMENT),
+        (dict(ws=A * 7 + 64), moe.MOE_ERR_ALIGNMENT),
+        (dict(h_in=A * 3 + 2), moe.MOE_ERR_ALIGNMENT),
+        (dict(ws_bytes=ws - 1), moe.MOE_ERR_WORKSPACE),
+        (dict(h_out=A * 2 + 256), moe.MOE_ERR_INVALID_ARG),  # overlaps h_in
+    ]
+    for over, code in cases:
+        a = dict(T=2, layer=A * 16, h_in=A * 2, h_out=A * 4, ws=A * 32, ws_bytes=ws)
+        a.update(over)
+        with pytest.raises(moe.MoeError) as e:
+            moe.moe_decode_layer(s, a["layer"], a["T"], a["h_in"], a["h_out"], None, None, a["ws"], a["ws_bytes"])
+        assert e.value.code == code, (over, e.value)
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_decode_stack(s, [A * 16, A * 16 + 64], 1, A * 2, A * 4, None, None, None, A * 32, ws)
+    assert e.value.code == moe.MOE_ERR_ALIGNMENT
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_decode_stack(s, [A * 16, 0], 1, A * 2, A * 4, None, None, None, A * 32, ws)
+    assert e.value.code == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_generate_layer(shape_of("tiny", expert_bits=5), 0, 0, A * 16)
+    assert e.value.code == moe.MOE_ERR_UNSUPPORTED
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_generate_layer(s, 0, 0, A * 16 + 4)
+    assert e.value.code == moe.MOE_ERR_ALIGNMENT
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 6, 8])
+@pytest.mark.parametrize("rows,cols", [(3, 64), (5, 192), (2, 1024)])
+def test_pack_matches_independent_reader(bits, rows, cols):
+    rng = np.random.default_rng(bits * 100 + cols)
+    codes = rng.integers(0, 2**bits, size=(rows, cols)).astype(np.uint8)
+    sc = rng.integers(0, 2**16, size=(rows, cols // 64)).astype(np.uint16)
+    bi = rng.integers(0, 2**16, size=(rows, cols // 64)).astype(np.uint16)
+    packed = moe.moe_pack_matrix(bits, codes, sc, bi)
+    assert packed.size == layout_ref.matrix_bytes(bits, rows, cols)
+    c2, s2, b2 = layout_ref.unpack(bits, rows, cols, packed)
+    assert np.array_equal(c2, codes) and np.array_equal(s2, sc) and np.array_equal(b2, bi)
+    c3, s3, b3 = moe.moe_unpack_matrix(bits, rows, cols, packed)
+    assert np.array_equal(c3, codes) and np.array_equal(s3, sc) and np.array_equal(b3, bi)
+
+
+def test_pack_known_words():
+    # 4 bits, LSB first: codes 1..8 in the first dword -> 0x87654321
+    codes = np.zeros((1, 64), dtype=np.uint8)
+    codes[0, :8] = np.arange(1, 9)
+    p = moe.moe_pack_matrix(4, codes, np.zeros((1, 1), np.uint16), np.zeros((1, 1), np.uint16))
+    assert p[:4].view(np.uint32)[0] == 0x87654321
+    # 3 bits: 10 codes of 7 fill bits 0..29 of the first dword
+    codes = np.zeros((1, 64), dtype=np.uint8)
+    codes[0, :10] = 7
+    p = moe.moe_pack_matrix(3, codes, np.zeros((1, 1), np.uint16), np.zeros((1, 1), np.uint16))
+    assert p[:8].view(np.uint32).tolist() == [0x3FFFFFFF, 0]
+    # 6 bits: code 63 at local index 5 -> low nibble at bits 20..23 of dword 0, high bits at 2*(0*4+1)+16 = 18
+    codes = np.zeros((1, 64), dtype=np.uint8)
+    codes[0, 5] = 63
+    p = moe.moe_pack_matrix(6, codes, np.zeros((1, 1), np.uint16), np.zeros((1, 1), np.uint16))
+    assert p[:12].view(np.uint32).tolist() == [0xF << 20, 0, 3 << 18]
+    # scale/bias dword: scale in the low half
+    p = moe.moe_pack_matrix(8, np.zeros((1, 64), np.uint8), np.array([[0x3F80]], np.uint16),
+                            np.array([[0xBF00]], np.uint16))
+    assert p[256:260].view(np.uint32)[0] == 0xBF003F80
+
+
+def test_pack_rejects_out_of_range_code():
+    codes = np.zeros((1, 64), dtype=np.uint8)
+    codes[0, 3] = 16
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_pack_matrix(4, codes, np.zeros((1, 1), np.uint16), np.zeros((1, 1), np.uint16))
+    assert e.value.code == moe.MOE_ERR_INVALID_ARG
