@@ -59,14 +59,16 @@ class DeviceStack:
         return out, ids, w
 
     def stack(self, h: torch.Tensor, n_layers: Optional[int] = None, trace: bool = False, routing: bool = True,
-              out: Optional[torch.Tensor] = None, bufs: Optional[Sequence[torch.Tensor]] = None):
+              out: Optional[torch.Tensor] = None, layer_ids: Optional[Sequence[int]] = None):
+        """Runs layers[0:n_layers] (or the listed layer indices) as one moe_decode_stack call."""
         T = h.shape[0]
-        n = n_layers or self.n_layers
+        sel = list(layer_ids) if layer_ids is not None else list(range(n_layers or self.n_layers))
+        n = len(sel)
         out = torch.empty_like(h) if out is None else out
         ids = torch.empty((n, T, self.k), dtype=torch.int32, device=self.device) if routing else None
         w = torch.empty((n, T, self.k), dtype=torch.float32, device=self.device) if routing else None
         tr = torch.empty((n + 1, T, self.H), dtype=torch.bfloat16, device=self.device) if trace else None
-        L.moe_decode_stack(self.shape, [b.data_ptr() for b in self.layers[:n]], T, h.data_ptr(), out.data_ptr(),
+        L.moe_decode_stack(self.shape, [self.layers[i].data_ptr() for i in sel], T, h.data_ptr(), out.data_ptr(),
                            None if ids is None else ids.data_ptr(), None if w is None else w.data_ptr(),
                            None if tr is None else tr.data_ptr(), self.ws.data_ptr(), self.ws_bytes, _stream())
         return out, ids, w, tr
@@ -75,3 +77,10 @@ class DeviceStack:
 def bf16_bits(t: torch.Tensor):
     """bf16 tensor -> numpy uint16 bit patterns (host copy)."""
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view("uint16")
+
+
+def bf16_from_bits(bits, device: str = "cuda:0") -> torch.Tensor:
+    """numpy uint16 bit patterns -> bf16 device tensor."""
+    import numpy as np
+
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
