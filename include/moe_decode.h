@@ -54,7 +54,7 @@ enum {
 };
 
 /* Shape of one MoE layer. Limits: hidden, inter, shared_inter multiples of 64
- * in [64, 16384]; 1 <= top_k <= min(n_experts, 16); n_experts <= 1024;
+ * in [64, 8192]; 1 <= top_k <= min(n_experts, 16); n_experts <= 512;
  * expert_bits, shared_bits in {2, 3, 4, 6, 8}; router_bits in {2, 3, 4, 6, 8}
  * or 16 (dense bf16 router); group must be 64; rms_eps > 0. */
 typedef struct moe_shape {

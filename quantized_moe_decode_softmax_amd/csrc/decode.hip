@@ -1,625 +1,525 @@
-// MoE decode kernels for gfx950 (wave64) and the moe_decode_layer /
-// moe_decode_stack entry points.
+// MoE decode kernels for gfx950 and the moe_decode_layer / moe_decode_stack
+// entry points.
 //
-// One layer runs as five stream-ordered kernels:
-//   router_kernel        raw router dot products W_r h_t for every (t, e)
-//   topk_kernel          RMS factor, shared gate, top-k, renormalised softmax
-//                        weights, and the deduplicated list of experts used by
-//                        any row (each expert's bytes are then read once per
-//                        call, however many rows select it)
-//   gateup_kernel        SwiGLU activations a = silu(r W_g h) * (r W_u h) for
-//                        every (unit, row using it); run for the routed units
-//                        and for the shared expert
-//   down_kernel          routed down projections W_d a, per (row, rank)
-//   down_combine_kernel  shared down projection, then the combine
-//                        h + sum_i w_i y_i + sigmoid-gate * y_s in rank order,
-//                        rounded to bf16 (nearest even)
-// The RMS factor r = 1/sqrt(mean(h^2) + eps) is applied after each dot
-// product: with RMSNorm weight 1, W (r h) = r (W h).
+// One layer is three stream-ordered kernels; each kernel boundary is one of
+// the layer's unavoidable all-to-all dependencies:
+//   route_kernel  (1 wave per workgroup) router dot products W_r h_t for every
+//                 token row t and expert, and, independent of routing, the
+//                 shared expert's SwiGLU activations; workgroup 0 also writes
+//                 the RMS factor r_t = 1/sqrt(mean(h_t^2) + eps) and the shared
+//                 expert's gate sigmoid(r_t gvec . h_t).
+//   expert_kernel every workgroup recomputes the routing (top-k of r_t W_r h_t,
+//                 ties to the lower id, softmax renormalised over the k) and
+//                 the sorted list of experts used by any row; its waves then
+//                 compute the SwiGLU activations silu(r W_g h) * (r W_u h) of
+//                 those experts, each expert's rows read once for all the
+//                 token rows that selected it.
+//   down_kernel   each workgroup owns a slice of output rows; one wave per
+//                 expert (routed and shared) computes W_d a for the rows that
+//                 use it; the slice is then combined in rank order:
+//                 h + sum_i w_i y_i + gate * y_shared, rounded to bf16
+//                 (nearest even).
+// RMSNorm has weight 1, so W (r h) = r (W h): h is used as stored (bf16) and
+// r multiplies each dot product. The activations a are kept as two bf16 parts
+// a = hi + lo (16 significant bits) so the down projections also run on
+// v_dot2c_f32_bf16.
 //
-// Dot products: a wave's lanes run along the input dimension in chunks of 32
-// codes (half a quantisation group). For 2/4/6-bit codes each pair of codes is
-// turned into a bf16 pair (128 + q_a, 128 + q_b) by one mask-and-or (the codes
-// land in the mantissa of 128.0) and multiplied with a bf16 pair of inputs by
-// v_dot2c_f32_bf16, so a chunk gives D = sum (128 + q) x; the group-affine
-// form then is s * D + (b - 128 s) * sum x. This is the flash-moe news page's
-// reordering ("FMA-optimised dequant kernel": code*(scale*x) + bias*x) taken
-// one step further: scale and bias are applied once per half-group instead of
-// once per weight. 8-bit codes (which do not fit a bf16 mantissa above 128)
-// use byte-to-float conversion and fp32 FMA. The down projections take the
-// fp32 activations as two bf16 parts a = hi + lo (16 significant bits).
+// Sources: PureDrive-35B-A3B-MLX model card, "Summary" (top-8 routed + shared
+// expert) and "How it works" (several token rows verified in one pass reading
+// the weights once; rows bit-identical to a one-row pass); flash-moe news page
+// (ja.news.hada.io topic 27758), "Metal Compute Shaders" (SwiGLU, RMS
+// normalisation, combine + residual + gate) and "Deferred GPU Expert Compute"
+// (combine and residual on the GPU, handed to the next layer directly).
 //
-// Determinism and row-exactness: every reduction has a fixed order, no
-// atomics touch data, and the arithmetic for one (row t, output) pair does not
-// depend on T or on which other rows share an expert.
+// Determinism and row-exactness: no atomics touch data, every reduction has a
+// fixed order, and the arithmetic of one (token row, output) pair is the same
+// whatever T is and whichever rows share an expert.
 #include <cmath>
 
-#include "device_common.h"
-#include "internal.h"
+#include "gemv.h"
 
 namespace moe {
 namespace {
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kMaxUnits = kMaxT * kMaxTopK;
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-constexpr uint32_t kMagic = 0x43004300u;  // bf16 pair (128.0, 128.0)
-constexpr uint32_t kOnes = 0x3F803F80u;   // bf16 pair (1.0, 1.0)
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-
-// bf16 pair from the same half of two words
-__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
-__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
-
-__host__ __device__ __forceinline__ int pow2ceil(int v) {
-  int p = 1;
-  while (p < v) p <<= 1;
-  return p;
-}
-__host__ __device__ __forceinline__ int lanes_per_row(int k) {
-  int n = pow2ceil(k / 32);
-  return n < 64 ? n : 64;
-}
-
-__device__ __forceinline__ void load16(const uint16_t* p, uint32_t (&w)[16]) {
-  const u32x4* q = (const u32x4*)p;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    u32x4 v = q[i];
-    w[4 * i] = v.x;
-    w[4 * i + 1] = v.y;
-    w[4 * i + 2] = v.z;
-    w[4 * i + 3] = v.w;
-  }
-}
-
-// x operand of one 32-code chunk: natural-order bf16 words (single) or hi/lo parts (split)
-template <bool SPLIT>
-struct XChunk {
-  uint32_t hi[16];
-  uint32_t lo[SPLIT ? 16 : 1];
+struct Dims {
+  int H, E, I, Is, k, T, imax;
+  int rbits, ebits, sbits;
+  float eps;
+  int64_t off_router, off_gatevec, off_shared, off_shared_up, off_shared_down;
+  int64_t off_e0, e_stride, off_e_up, off_e_down;
 };
 
-// D = sum_j (128 + q_j) x_j over a 32-code chunk, bits 2/4/6, from packed words w.
-template <int BITS>
-__device__ __forceinline__ float magic_dot(const uint32_t* w, const uint32_t (&x)[16], float acc) {
-  if constexpr (BITS == 4) {
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t q = ((w[d] >> (4 * i)) & 0x000F000Fu) | kMagic;
-        const uint32_t a = x[4 * d + (i >> 1)], b = x[4 * d + 2 + (i >> 1)];
-        acc = dot2(q, (i & 1) ? pair_hi(a, b) : pair_lo(a, b), acc);
-      }
-  } else if constexpr (BITS == 6) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint32_t hw = w[3 * u + 2];
-#pragma unroll
-      for (int d = 0; d < 2; ++d)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int sh = 2 * (4 * d + i) - 4;
-          const uint32_t hs = sh >= 0 ? (hw >> sh) : (hw << (-sh));
-          const uint32_t q = (((w[3 * u + d] >> (4 * i)) & 0x000F000Fu) | kMagic) | (hs & 0x00300030u);
-          const int dd = 2 * u + d;
-          const uint32_t a = x[4 * dd + (i >> 1)], b = x[4 * dd + 2 + (i >> 1)];
-          acc = dot2(q, (i & 1) ? pair_hi(a, b) : pair_lo(a, b), acc);
-        }
-    }
-  } else {  // BITS == 2
-#pragma unroll
-    for (int d = 0; d < 2; ++d)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t q = ((w[d] >> (2 * i)) & 0x00030003u) | kMagic;
-        const uint32_t a = x[8 * d + (i >> 1)], b = x[8 * d + 4 + (i >> 1)];
-        acc = dot2(q, (i & 1) ? pair_hi(a, b) : pair_lo(a, b), acc);
-      }
-  }
-  return acc;
-}
-
-__device__ __forceinline__ float sum_pairs(const uint32_t (&x)[16], float acc) {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) acc = dot2(x[i], kOnes, acc);
-  return acc;
-}
-
-// sum_j q_j x_j for 8-bit codes (4 per dword, byte j%4), x from bf16 words
-__device__ __forceinline__ float byte_dot(const uint32_t* w, const uint32_t (&x)[16], float acc) {
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const uint32_t v = w[k];
-    const uint32_t xa = x[2 * k], xb = x[2 * k + 1];
-    acc = fmaf((float)(v & 0xFFu), bf16_lo_to_f32(xa), acc);
-    acc = fmaf((float)((v >> 8) & 0xFFu), bf16_hi_to_f32(xa), acc);
-    acc = fmaf((float)((v >> 16) & 0xFFu), bf16_lo_to_f32(xb), acc);
-    acc = fmaf((float)(v >> 24), bf16_hi_to_f32(xb), acc);
-  }
-  return acc;
-}
-
-// sum_j q_j x_j for 3-bit codes (10 per dword), codes 32c .. 32c+31 of the row
-__device__ __forceinline__ float tri_dot(const uint32_t* row, int c, const uint32_t (&x)[16], float acc) {
-#pragma unroll 4
-  for (int i = 0; i < 32; ++i) {
-    const int j = 32 * c + i;
-    const uint32_t q = (row[j / 10] >> (3 * (j % 10))) & 7u;
-    const uint32_t xw = x[i >> 1];
-    acc = fmaf((float)q, (i & 1) ? bf16_hi_to_f32(xw) : bf16_lo_to_f32(xw), acc);
-  }
-  return acc;
-}
-
-template <int BITS>
-__device__ __forceinline__ void load_codes(const uint8_t* row, int c, uint32_t* w) {
-  if constexpr (BITS == 2) {
-    u32x2 v = *(const u32x2*)(row + 8 * c);
-    w[0] = v.x;
-    w[1] = v.y;
-  } else if constexpr (BITS == 4) {
-    u32x4 v = *(const u32x4*)(row + 16 * c);
-    w[0] = v.x;
-    w[1] = v.y;
-    w[2] = v.z;
-    w[3] = v.w;
-  } else if constexpr (BITS == 6) {
-    const u32x2* p = (const u32x2*)(row + 24 * c);
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      u32x2 v = p[i];
-      w[2 * i] = v.x;
-      w[2 * i + 1] = v.y;
-    }
-  } else if constexpr (BITS == 8) {
-    const u32x4* p = (const u32x4*)(row + 32 * c);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      u32x4 v = p[i];
-      w[4 * i] = v.x;
-      w[4 * i + 1] = v.y;
-      w[4 * i + 2] = v.z;
-      w[4 * i + 3] = v.w;
-    }
-  }
-}
-
-// Partial dot product of one lane: sum over its chunks (c = li, li + lpr, ...)
-// of s*D + b_eff*sum(x). Quantised matrix with `BITS`, K columns, row `r`.
-// x: bf16 [K] (SPLIT = false) or hi/lo bf16 [K] each (SPLIT = true).
-template <int BITS, bool SPLIT>
-__device__ float lane_partial(const uint8_t* codes, const uint32_t* sb, int64_t rb, int r, int K, const uint16_t* xhi,
-                              const uint16_t* xlo, int li, int lpr) {
-  float acc = 0.f;
-  const int nch = K >> 5;
-  const uint8_t* row = codes + (int64_t)r * rb;
-  const uint32_t* sbr = sb + (int64_t)r * (K >> 6);
-  for (int c = li; c < nch; c += lpr) {
-    XChunk<SPLIT> xc;
-    load16(xhi + 32 * c, xc.hi);
-    if constexpr (SPLIT) load16(xlo + 32 * c, xc.lo);
-    const uint32_t sbw = sbr[c >> 1];
-    const float s = bf16_lo_to_f32(sbw), b = bf16_hi_to_f32(sbw);
-    float d, sx;
-    if constexpr (BITS == 2 || BITS == 4 || BITS == 6) {
-      uint32_t w[6];
-      load_codes<BITS>(row, c, w);
-      d = magic_dot<BITS>(w, xc.hi, 0.f);
-      sx = sum_pairs(xc.hi, 0.f);
-      if constexpr (SPLIT) {
-        d += magic_dot<BITS>(w, xc.lo, 0.f);
-        sx += sum_pairs(xc.lo, 0.f);
-      }
-      acc += fmaf(s, d, (b - 128.f * s) * sx);
-    } else {
-      if constexpr (BITS == 8) {
-        uint32_t w[8];
-        load_codes<8>(row, c, w);
-        d = byte_dot(w, xc.hi, 0.f);
-        if constexpr (SPLIT) d += byte_dot(w, xc.lo, 0.f);
-      } else {
-        d = tri_dot((const uint32_t*)row, c, xc.hi, 0.f);
-        if constexpr (SPLIT) d += tri_dot((const uint32_t*)row, c, xc.lo, 0.f);
-      }
-      sx = sum_pairs(xc.hi, 0.f);
-      if constexpr (SPLIT) sx += sum_pairs(xc.lo, 0.f);
-      acc += fmaf(s, d, b * sx);
-    }
-  }
-  return acc;
-}
-
-// Partial dot product of one lane for a dense bf16 matrix row (router_bits 16).
-__device__ float lane_partial_dense(const uint16_t* wmat, int r, int K, const uint16_t* x, int li, int lpr) {
-  float acc = 0.f;
-  const int nch = K >> 5;
-  for (int c = li; c < nch; c += lpr) {
-    uint32_t w[16], xw[16];
-    load16(wmat + (int64_t)r * K + 32 * c, w);
-    load16(x + 32 * c, xw);
-    float d = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) d = dot2(w[i], xw[i], d);
-    acc += d;
-  }
-  return acc;
-}
-
-__device__ __forceinline__ float reduce_lanes(float v, int lpr) {
-  for (int off = 1; off < lpr; off <<= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
-// ------------------------------------------------------------------ router
-template <int RB>
-__global__ void __launch_bounds__(kThreads) router_kernel(const uint8_t* layer, int64_t off, int E, int H, int T,
-                                                          const uint16_t* h, float* raw) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lpr = lanes_per_row(H), rpw = 64 / lpr;
-  const int sr = lane / lpr, li = lane % lpr;
-  const int rows_per_iter = gridDim.x * kWaves * rpw;
-  for (int base = (blockIdx.x * kWaves + wave) * rpw; base < E; base += rows_per_iter) {
-    const int e = base + sr;
-    const bool ok = e < E;
-    const int er = ok ? e : 0;
-    for (int t = 0; t < T; ++t) {
-      float p;
-      if constexpr (RB == 16) {
-        p = lane_partial_dense((const uint16_t*)(layer + off), er, H, h + (int64_t)t * H, li, lpr);
-      } else {
-        const uint8_t* codes = layer + off;
-        const uint32_t* sb = (const uint32_t*)(codes + matrix_codes_bytes(RB, E, H));
-        p = lane_partial<RB, false>(codes, sb, row_bytes(RB, H), er, H, h + (int64_t)t * H, nullptr, li, lpr);
-      }
-      p = reduce_lanes(p, lpr);
-      if (ok && li == 0) raw[(int64_t)t * E + e] = p;
-    }
-  }
-}
-
-// ------------------------------------------------------------------- top-k
-struct Best {
-  float v;
-  int i;
+struct Ptrs {
+  const uint8_t* layer;
+  const uint16_t* h_in;
+  uint16_t* h_out;
+  int32_t* ids_out;
+  float* w_out;
+  float* raw;
+  float* rinv;
+  float* sg;
+  int* ids;
+  float* wts;
+  int* units;
+  uint32_t* masks;
+  uint16_t* a_hi;
+  uint16_t* a_lo;
 };
-__device__ __forceinline__ bool better(float av, int ai, float bv, int bi) { return av > bv || (av == bv && ai < bi); }
 
-__device__ float block_sum(float v, float* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float s = red[0];
-  for (int w = 1; w < kWaves; ++w) s += red[w];
-  return s;
+__device__ __forceinline__ float silu_mul(float g, float v) { return g / (1.0f + expf(-g)) * v; }
+
+__device__ __forceinline__ float rms_factor(float sumsq, int H, float eps) { return 1.0f / sqrtf(sumsq / (float)H + eps); }
+
+__device__ __forceinline__ void store_a(const Dims& d, const Ptrs& p, int t, int slot, int i, float a) {
+  const uint32_t hb = __float_as_uint(a) & 0xFFFF0000u;
+  const int64_t idx = ((int64_t)t * (d.k + 1) + slot) * d.imax + i;
+  p.a_hi[idx] = (uint16_t)(hb >> 16);
+  p.a_lo[idx] = (uint16_t)f32_to_bf16_rne(a - __uint_as_float(hb));
 }
 
-__global__ void __launch_bounds__(kThreads) topk_kernel(const uint16_t* gvec, int E, int H, int k, int T, float eps,
-                                                        const uint16_t* h, const float* raw, float* rinv, float* sgate,
-                                                        int* ids_ws, float* w_ws, int* units, uint32_t* masks,
-                                                        int* ids_out, float* w_out) {
-  __shared__ float lam[kMaxExperts];
-  __shared__ uint32_t emask[kMaxExperts];
-  __shared__ unsigned char taken[kMaxExperts];
-  __shared__ float red[kWaves];
-  __shared__ float bv[kWaves];
-  __shared__ int bi[kWaves];
-  __shared__ float selv[kMaxTopK];
-  __shared__ int seli[kMaxTopK];
-  __shared__ int wave_cnt[kWaves];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < E; e += kThreads) emask[e] = 0u;
-  for (int t = 0; t < T; ++t) {
-    const uint16_t* ht = h + (int64_t)t * H;
-    float ss = 0.f, gd = 0.f;
-    for (int j = tid; j < H; j += kThreads) {
-      const float x = __uint_as_float((uint32_t)ht[j] << 16);
-      ss = fmaf(x, x, ss);
-      gd = fmaf(x, __uint_as_float((uint32_t)gvec[j] << 16), gd);
-    }
-    ss = block_sum(ss, red);
-    gd = block_sum(gd, red);
-    const float r = 1.0f / sqrtf(ss / (float)H + eps);
-    const float sg = 1.0f / (1.0f + expf(-(r * gd)));
-    for (int e = tid; e < E; e += kThreads) {
-      lam[e] = r * raw[(int64_t)t * E + e];
-      taken[e] = 0;
-    }
-    __syncthreads();
-    for (int i = 0; i < k; ++i) {
-      float v = -INFINITY;
-      int vi = 0x7FFFFFFF;
-      for (int e = tid; e < E; e += kThreads)
-        if (!taken[e] && better(lam[e], e, v, vi)) {
-          v = lam[e];
-          vi = e;
-        }
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(v, off, 64);
-        const int oi = __shfl_xor(vi, off, 64);
-        if (better(ov, oi, v, vi)) {
-          v = ov;
-          vi = oi;
-        }
-      }
-      if (lane == 0) {
-        bv[wave] = v;
-        bi[wave] = vi;
-      }
-      __syncthreads();
-      if (tid == 0) {
-        float b = bv[0];
-        int bidx = bi[0];
-        for (int w = 1; w < kWaves; ++w)
-          if (better(bv[w], bi[w], b, bidx)) {
-            b = bv[w];
-            bidx = bi[w];
-          }
-        selv[i] = b;
-        seli[i] = bidx;
-        taken[bidx] = 1;
-      }
-      __syncthreads();
-    }
-    if (tid == 0) {
-      const float m = selv[0];
-      float ex[kMaxTopK];
-      float sum = 0.f;
-      for (int i = 0; i < k; ++i) {
-        ex[i] = expf(selv[i] - m);
-        sum += ex[i];
-      }
-      for (int i = 0; i < k; ++i) {
-        const float w = ex[i] / sum;
-        ids_ws[t * k + i] = seli[i];
-        w_ws[t * k + i] = w;
-        if (ids_out) ids_out[t * k + i] = seli[i];
-        if (w_out) w_out[t * k + i] = w;
-        emask[seli[i]] |= 1u << t;
-      }
-      rinv[t] = r;
-      sgate[t] = sg;
-    }
-    __syncthreads();
+// rows per lane group of one wave task, by chunks per lane
+template <int CPL>
+struct TaskRows {
+  static constexpr int R = CPL >= 2 ? 2 : 4;  // rows loaded per lane group
+};
+
+// RMS factor and shared-expert gate of token row t (written once per call).
+// ss: sum of squares of the row (valid in the group's last lane).
+__device__ __forceinline__ void row_stats(const Dims& d, const Ptrs& p, int t, int li, int lpr, float ss) {
+  const uint16_t* gv = (const uint16_t*)(p.layer + d.off_gatevec);
+  const uint16_t* ht = p.h_in + (int64_t)t * d.H;
+  const int nch = d.H >> 5;
+  float gd = 0.f;
+  for (int c = li; c < nch; c += lpr) {
+    uint32_t hw[16], gw[16];
+    load64B(ht + 32 * c, hw);
+    load64B(gv + 32 * c, gw);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) gd = dot2(hw[i], gw[i], gd);
   }
-  // compact the experts used by any row, in ascending id order
-  int base = 0;
-  for (int e0 = 0; e0 < E; e0 += kThreads) {
-    const int e = e0 + tid;
-    const bool used = e < E && emask[e] != 0u;
-    const unsigned long long bal = __ballot(used);
-    const int before = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) wave_cnt[wave] = __popcll(bal);
-    __syncthreads();
-    int off = base;
-    for (int w = 0; w < wave; ++w) off += wave_cnt[w];
-    if (used) {
-      units[1 + off + before] = e;
-      masks[off + before] = emask[e];
-    }
-    int tot = 0;
-    for (int w = 0; w < kWaves; ++w) tot += wave_cnt[w];
-    base += tot;
-    __syncthreads();
+  gd = reduce_row(gd, lpr);
+  const int lane = threadIdx.x & 63;
+  if (lane == lpr - 1) {
+    const float r = rms_factor(ss, d.H, d.eps);
+    p.rinv[t] = r;
+    p.sg[t] = 1.0f / (1.0f + expf(-(r * gd)));
   }
-  if (tid == 0) units[0] = base;
 }
 
-// ---------------------------------------------------------------- gate/up
-// grid: (row blocks, units). shared == 1: one unit, the shared expert, used by
-// every row, activations go to slot k. Otherwise unit y is the y-th entry of
-// the deduplicated list (blocks beyond the count exit).
-template <int BITS>
-__global__ void __launch_bounds__(kThreads) gateup_kernel(const uint8_t* layer, int64_t off_e, int64_t stride,
-                                                          int64_t off_up, int I, int H, int k, int T, int shared,
-                                                          int rows_per_block, const uint16_t* h, const float* rinv,
-                                                          const int* ids_ws, const int* units, const uint32_t* masks,
-                                                          uint16_t* a_hi, uint16_t* a_lo, int imax) {
-  int e = 0;
-  uint32_t mask;
-  if (shared) {
-    mask = T >= 32 ? 0xFFFFFFFFu : ((1u << T) - 1u);
+// ----------------------------------------------------------- route kernel
+template <int BITS, int CPL>
+__device__ __forceinline__ void router_task(const Dims& d, const Ptrs& p, int task, int li, int lpr, int sr, int rpw) {
+  constexpr int R = TaskRows<CPL>::R;
+  int rows[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int e = task * R * rpw + sr + rpw * r;
+    rows[r] = e < d.E ? e : -1;
+  }
+  float out[R];
+  if constexpr (BITS == kDense) {
+    XLane<kDense, CPL> x;
+    const uint16_t* w = (const uint16_t*)(p.layer + d.off_router);
+    const uint16_t* rp[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) rp[r] = rows[r] >= 0 ? w + (int64_t)rows[r] * d.H : nullptr;
+    RowsD<CPL, R> Q;
+    load_dense_rows<CPL, R>(Q, rp, d.H, li, lpr);
+    for (int t = 0; t < d.T; ++t) {
+      prep_x<kDense, CPL>(x, p.h_in + (int64_t)t * d.H, d.H, li, lpr);
+      if (task == 0) row_stats(d, p, t, li, lpr, reduce_row(sumsq(x), lpr));
+      dot_dense_rows<CPL, R>(Q, x, out);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float v = reduce_row(out[r], lpr);
+        if (rows[r] >= 0 && li == lpr - 1) p.raw[(int64_t)t * d.E + rows[r]] = v;
+      }
+    }
   } else {
-    if ((int)blockIdx.y >= units[0]) return;
-    e = units[1 + blockIdx.y];
-    mask = masks[blockIdx.y];
-  }
-  const uint8_t* gate = layer + off_e + (int64_t)e * stride;
-  const uint8_t* up = gate + off_up;
-  const uint32_t* gsb = (const uint32_t*)(gate + matrix_codes_bytes(BITS, I, H));
-  const uint32_t* usb = (const uint32_t*)(up + matrix_codes_bytes(BITS, I, H));
-  const int64_t rb = row_bytes(BITS, H);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lpr = lanes_per_row(H), rpw = 64 / lpr;
-  const int sr = lane / lpr, li = lane % lpr;
-  const int r0 = blockIdx.x * rows_per_block;
-  int r1 = r0 + rows_per_block;
-  if (r1 > I) r1 = I;
-  for (int t = 0; t < T; ++t) {
-    if (!(mask >> t & 1u)) continue;
-    int slot = k;
-    if (!shared)
-      for (int i = 0; i < k; ++i)
-        if (ids_ws[t * k + i] == e) slot = i;
-    const float r = rinv[t];
-    const uint16_t* ht = h + (int64_t)t * H;
-    for (int base = r0 + wave * rpw; base < r1; base += kWaves * rpw) {
-      const int row = base + sr;
-      const bool ok = row < r1;
-      const int rr = ok ? row : r0;
-      float g = lane_partial<BITS, false>(gate, gsb, rb, rr, H, ht, nullptr, li, lpr);
-      float v = lane_partial<BITS, false>(up, usb, rb, rr, H, ht, nullptr, li, lpr);
-      g = reduce_lanes(g, lpr) * r;
-      v = reduce_lanes(v, lpr) * r;
-      if (ok && li == 0) {
-        const float a = g / (1.0f + expf(-g)) * v;
-        const uint32_t hb = __float_as_uint(a) & 0xFFFF0000u;
-        const float lo = a - __uint_as_float(hb);
-        const int64_t idx = ((int64_t)t * (k + 1) + slot) * imax + row;
-        a_hi[idx] = (uint16_t)(hb >> 16);
-        a_lo[idx] = (uint16_t)f32_to_bf16_rne(lo);
+    const uint8_t* base = p.layer + d.off_router;
+    const int64_t rb = row_bytes(BITS, d.H);
+    const uint32_t* sb = (const uint32_t*)(base + matrix_codes_bytes(BITS, d.E, d.H));
+    const uint8_t* rc[R];
+    const uint32_t* rs[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      rc[r] = rows[r] >= 0 ? base + (int64_t)rows[r] * rb : nullptr;
+      rs[r] = rows[r] >= 0 ? sb + (int64_t)rows[r] * (d.H >> 6) : nullptr;
+    }
+    RowsQ<BITS, CPL, R> Q;
+    load_rows<BITS, CPL, R>(Q, rc, rs, d.H, (int)(rb >> 2), li, lpr);
+    XLane<BITS, CPL> x;
+    for (int t = 0; t < d.T; ++t) {
+      prep_x<BITS, CPL>(x, p.h_in + (int64_t)t * d.H, d.H, li, lpr);
+      if (task == 0) row_stats(d, p, t, li, lpr, reduce_row(sumsq(x), lpr));
+      dot_rows<BITS, CPL, R, 1>(Q, x, x, out);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float v = reduce_row(out[r], lpr);
+        if (rows[r] >= 0 && li == lpr - 1) p.raw[(int64_t)t * d.E + rows[r]] = v;
       }
     }
   }
 }
 
-// ------------------------------------------------------------------- down
-// Routed down projections: dsum[t][slot][j] = (W_d,e a[t][slot])_j.
-template <int BITS>
-__global__ void __launch_bounds__(kThreads) down_kernel(const uint8_t* layer, int64_t off_e, int64_t stride,
-                                                        int64_t off_down, int I, int H, int k, int T,
-                                                        int rows_per_block, const int* ids_ws, const int* units,
-                                                        const uint32_t* masks, const uint16_t* a_hi,
-                                                        const uint16_t* a_lo, int imax, float* dsum) {
-  if ((int)blockIdx.y >= units[0]) return;
-  const int e = units[1 + blockIdx.y];
-  const uint32_t mask = masks[blockIdx.y];
-  const uint8_t* down = layer + off_e + (int64_t)e * stride + off_down;
-  const uint32_t* dsb = (const uint32_t*)(down + matrix_codes_bytes(BITS, H, I));
-  const int64_t rb = row_bytes(BITS, I);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lpr = lanes_per_row(I), rpw = 64 / lpr;
-  const int sr = lane / lpr, li = lane % lpr;
-  const int r0 = blockIdx.x * rows_per_block;
-  int r1 = r0 + rows_per_block;
-  if (r1 > H) r1 = H;
-  for (int t = 0; t < T; ++t) {
-    if (!(mask >> t & 1u)) continue;
-    int slot = 0;
-    for (int i = 0; i < k; ++i)
-      if (ids_ws[t * k + i] == e) slot = i;
-    const int64_t aoff = ((int64_t)t * (k + 1) + slot) * imax;
-    for (int base = r0 + wave * rpw; base < r1; base += kWaves * rpw) {
-      const int row = base + sr;
-      const bool ok = row < r1;
-      float p = lane_partial<BITS, true>(down, dsb, rb, ok ? row : r0, I, a_hi + aoff, a_lo + aoff, li, lpr);
-      p = reduce_lanes(p, lpr);
-      if (ok && li == 0) dsum[((int64_t)t * k + slot) * H + row] = p;
+// SwiGLU rows of one expert block (gate rows [0, I), up rows at +off_up):
+// task covers pairs i = i0 + sr + rpw * r. rowmask: token rows using it.
+template <int BITS, int CPL>
+__device__ __forceinline__ void swiglu_task(const Dims& d, const Ptrs& p, const uint8_t* blk, int64_t off_up, int I, int i0,
+                            uint32_t rowmask, int slot_fixed, int e, const int* s_ids, const float* rinv, int li,
+                            int lpr, int sr, int rpw) {
+  constexpr int RP = TaskRows<CPL>::R / 2;  // pairs per lane group
+  constexpr int R = 2 * RP;
+  const int64_t rb = row_bytes(BITS, d.H);
+  const int64_t cb = matrix_codes_bytes(BITS, I, d.H);
+  const uint8_t* gate = blk;
+  const uint8_t* up = blk + off_up;
+  const uint32_t* gsb = (const uint32_t*)(gate + cb);
+  const uint32_t* usb = (const uint32_t*)(up + cb);
+  int pairs[RP];
+  const uint8_t* rc[R];
+  const uint32_t* rs[R];
+#pragma unroll
+  for (int r = 0; r < RP; ++r) {
+    const int i = i0 + sr + rpw * r;
+    pairs[r] = i < I ? i : -1;
+    rc[r] = i < I ? gate + (int64_t)i * rb : nullptr;
+    rs[r] = i < I ? gsb + (int64_t)i * (d.H >> 6) : nullptr;
+    rc[RP + r] = i < I ? up + (int64_t)i * rb : nullptr;
+    rs[RP + r] = i < I ? usb + (int64_t)i * (d.H >> 6) : nullptr;
+  }
+  RowsQ<BITS, CPL, R> Q;
+  load_rows<BITS, CPL, R>(Q, rc, rs, d.H, (int)(rb >> 2), li, lpr);
+  XLane<BITS, CPL> x;
+  float out[R];
+  for (int t = 0; t < d.T; ++t) {
+    if (!(rowmask >> t & 1u)) continue;
+    int slot = slot_fixed;
+    if (slot < 0)
+      for (int i = 0; i < d.k; ++i)
+        if (s_ids[t * kMaxTopK + i] == e) slot = i;
+    prep_x<BITS, CPL>(x, p.h_in + (int64_t)t * d.H, d.H, li, lpr);
+    dot_rows<BITS, CPL, R, 1>(Q, x, x, out);
+    // RMS factor: from the workspace, or from the same x chunks (lanes of a
+    // row group cover the whole row)
+    const float r = rinv ? rinv[t] : rms_factor(reduce_row(sumsq(x), lpr), d.H, d.eps);
+#pragma unroll
+    for (int q = 0; q < RP; ++q) {
+      const float g = reduce_row(out[q], lpr) * r;
+      const float v = reduce_row(out[RP + q], lpr) * r;
+      if (pairs[q] >= 0 && li == lpr - 1) store_a(d, p, t, slot, pairs[q], silu_mul(g, v));
     }
   }
 }
 
-// Shared down projection + combine + residual + bf16 output.
-template <int BITS>
-__global__ void __launch_bounds__(kThreads) down_combine_kernel(const uint8_t* layer, int64_t off_s, int64_t off_down,
-                                                                int Is, int H, int k, int T, int rows_per_block,
-                                                                const uint16_t* h, const float* wts, const float* sgate,
-                                                                const uint16_t* a_hi, const uint16_t* a_lo, int imax,
-                                                                const float* dsum, uint16_t* h_out) {
-  const uint8_t* down = layer + off_s + off_down;
-  const uint32_t* dsb = (const uint32_t*)(down + matrix_codes_bytes(BITS, H, Is));
-  const int64_t rb = row_bytes(BITS, Is);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lpr = lanes_per_row(Is), rpw = 64 / lpr;
-  const int sr = lane / lpr, li = lane % lpr;
-  const int r0 = blockIdx.x * rows_per_block;
-  int r1 = r0 + rows_per_block;
-  if (r1 > H) r1 = H;
-  for (int t = 0; t < T; ++t) {
-    const int64_t aoff = ((int64_t)t * (k + 1) + k) * imax;
-    for (int base = r0 + wave * rpw; base < r1; base += kWaves * rpw) {
-      const int row = base + sr;
-      const bool ok = row < r1;
-      float p = lane_partial<BITS, true>(down, dsb, rb, ok ? row : r0, Is, a_hi + aoff, a_lo + aoff, li, lpr);
-      p = reduce_lanes(p, lpr);
-      if (ok && li == 0) {
-        float acc = 0.f;
-        for (int i = 0; i < k; ++i) acc = fmaf(wts[t * k + i], dsum[((int64_t)t * k + i) * H + row], acc);
-        acc = fmaf(sgate[t], p, acc);
-        const float out = __uint_as_float((uint32_t)h[(int64_t)t * H + row] << 16) + acc;
-        h_out[(int64_t)t * H + row] = (uint16_t)f32_to_bf16_rne(out);
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------- dispatch
-int blocks_for(int rows, int rows_per_block) { return (rows + rows_per_block - 1) / rows_per_block; }
-
-int rows_per_block_for(int k_dim, int passes) { return kWaves * (64 / lanes_per_row(k_dim)) * passes; }
-
-#define MOE_BITS_SWITCH(bits, B, ...)               \
-  switch (bits) {                                   \
+#define MOE_BITS_CASES(bits, B, ...)                   \
+  switch (bits) {                                      \
     case 2: { constexpr int B = 2; __VA_ARGS__; } break; \
     case 3: { constexpr int B = 3; __VA_ARGS__; } break; \
     case 4: { constexpr int B = 4; __VA_ARGS__; } break; \
     case 6: { constexpr int B = 6; __VA_ARGS__; } break; \
-    case 8: { constexpr int B = 8; __VA_ARGS__; } break; \
-    default: break;                                 \
+    default: { constexpr int B = 8; __VA_ARGS__; } break; \
   }
 
-struct LayerCall {
-  const moe_shape_t* s;
-  moe_layer_layout_t L;
-  WsMap m;
-  uint8_t* ws;
-  int T;
-};
-
-int32_t launch_layer(const LayerCall& c, const uint8_t* layer, const uint16_t* h_in, uint16_t* h_out, int32_t* ids_out,
-                     float* w_out, hipStream_t st) {
-  const moe_shape_t& s = *c.s;
-  const WsMap& m = c.m;
-  uint8_t* ws = c.ws;
-  const int T = c.T, E = s.n_experts, H = s.hidden, k = s.top_k;
-  const int max_units = T * k < E ? T * k : E;
-  const int imax = s.inter > s.shared_inter ? s.inter : s.shared_inter;
-  float* raw = (float*)(ws + m.raw_logits);
-  float* rinv = (float*)(ws + m.rinv);
-  float* sg = (float*)(ws + m.sgate);
-  int* ids = (int*)(ws + m.ids);
-  float* wts = (float*)(ws + m.wts);
-  int* units = (int*)(ws + m.units);
-  uint32_t* masks = (uint32_t*)(ws + m.masks);
-  uint16_t* a_hi = (uint16_t*)(ws + m.a_hi);
-  uint16_t* a_lo = (uint16_t*)(ws + m.a_lo);
-  float* dsum = (float*)(ws + m.dsum);
-
-  {  // router
-    const int rpb = rows_per_block_for(H, 1);
-    const int g = blocks_for(E, rpb);
-    if (s.router_bits == 16) {
-      router_kernel<16><<<g, kThreads, 0, st>>>(layer, c.L.router, E, H, T, h_in, raw);
+// grid: n_router_tasks + n_shared_tasks workgroups of one wave.
+template <int CPL>
+__global__ void __launch_bounds__(64, 2) route_kernel(Dims d, Ptrs p, int n_rt) {
+  const int lane = threadIdx.x, task = blockIdx.x;
+  const int lpr = lanes_per_row(d.H), rpw = 64 / lpr, sr = lane / lpr, li = lane % lpr;
+  if (task < n_rt) {
+    if (d.rbits == kDense) {
+      router_task<kDense, CPL>(d, p, task, li, lpr, sr, rpw);
     } else {
-      MOE_BITS_SWITCH(s.router_bits, B, router_kernel<B><<<g, kThreads, 0, st>>>(layer, c.L.router, E, H, T, h_in, raw));
+      MOE_BITS_CASES(d.rbits, B, router_task<B, CPL>(d, p, task, li, lpr, sr, rpw));
+    }
+  } else {
+    constexpr int RP = TaskRows<CPL>::R / 2;
+    const int i0 = (task - n_rt) * RP * rpw;
+    const uint32_t all = d.T >= 32 ? 0xFFFFFFFFu : ((1u << d.T) - 1u);
+    MOE_BITS_CASES(d.sbits, B,
+                   swiglu_task<B, CPL>(d, p, p.layer + d.off_shared, d.off_shared_up, d.Is, i0, all, d.k, -1, nullptr,
+                                       nullptr, li, lpr, sr, rpw));
+  }
+}
+
+// ---------------------------------------------------------- expert kernel
+template <int CPL>
+__global__ void __launch_bounds__(256, 2) expert_kernel(Dims d, Ptrs p, int tasks_per_unit) {
+  __shared__ int s_ids[kMaxT * kMaxTopK];
+  __shared__ float s_w[kMaxT * kMaxTopK];
+  __shared__ float s_r[kMaxT];
+  __shared__ uint32_t s_emask[kMaxExperts];
+  __shared__ int s_units[kMaxUnits];
+  __shared__ uint32_t s_masks[kMaxUnits];
+  __shared__ int s_wcnt[4];
+  __shared__ int s_nunits;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < d.E; e += 256) s_emask[e] = 0u;
+  __syncthreads();
+  // routing of every token row (row t on wave t % 4)
+  for (int t = wave; t < d.T; t += 4) {
+    int ids[kMaxTopK];
+    float w[kMaxTopK];
+    float r;
+    wave_topk(p.raw + (int64_t)t * d.E, p.rinv + t, d.E, d.k, ids, w, r);
+    // lane i publishes entry i
+    const int my_id = lane_pick(ids, lane);
+    const float my_w = lane_pick(w, lane);
+    if (lane < d.k) {
+      s_ids[t * kMaxTopK + lane] = my_id;
+      s_w[t * kMaxTopK + lane] = my_w;
+      atomicOr(&s_emask[my_id], 1u << t);
+    }
+    if (lane == 0) s_r[t] = r;
+  }
+  __syncthreads();
+  // experts used by any row, ascending
+  int base = 0;
+  for (int e0 = 0; e0 < d.E; e0 += 256) {
+    const int e = e0 + tid;
+    const bool used = e < d.E && s_emask[e] != 0u;
+    const unsigned long long bal = __ballot(used);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) s_wcnt[wave] = __popcll(bal);
+    __syncthreads();
+    int off = base;
+    for (int w = 0; w < wave; ++w) off += s_wcnt[w];
+    if (used) {
+      s_units[off + before] = e;
+      s_masks[off + before] = s_emask[e];
+    }
+    base += s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
+    __syncthreads();
+  }
+  const int n_units = base;
+  if (blockIdx.x == 0) {
+    for (int i = tid; i < d.T * d.k; i += 256) {
+      const int t = i / d.k, j = i % d.k;
+      p.ids[i] = s_ids[t * kMaxTopK + j];
+      p.wts[i] = s_w[t * kMaxTopK + j];
+      if (p.ids_out) p.ids_out[i] = s_ids[t * kMaxTopK + j];
+      if (p.w_out) p.w_out[i] = s_w[t * kMaxTopK + j];
+    }
+    for (int u = tid; u < n_units; u += 256) {
+      p.units[1 + u] = s_units[u];
+      p.masks[u] = s_masks[u];
+    }
+    if (tid == 0) p.units[0] = n_units;
+  }
+  (void)s_nunits;
+  // SwiGLU tasks: (unit, block of row pairs)
+  const int lpr = lanes_per_row(d.H), rpw = 64 / lpr, sr = lane / lpr, li = lane % lpr;
+  constexpr int RP = TaskRows<CPL>::R / 2;
+  const int n_tasks = n_units * tasks_per_unit;
+  for (int task = blockIdx.x * 4 + wave; task < n_tasks; task += gridDim.x * 4) {
+    const int u = task / tasks_per_unit;
+    const int i0 = (task % tasks_per_unit) * RP * rpw;
+    const int e = s_units[u];
+    const uint8_t* blk = p.layer + d.off_e0 + (int64_t)e * d.e_stride;
+    MOE_BITS_CASES(d.ebits, B,
+                   swiglu_task<B, CPL>(d, p, blk, d.off_e_up, d.I, i0, s_masks[u], -1, e, s_ids, s_r, li, lpr, sr,
+                                       rpw));
+  }
+}
+
+// ------------------------------------------------------------ down kernel
+template <int BITS, int CPL, int RD>
+__device__ __forceinline__ void down_unit(const Dims& d, const Ptrs& p, const uint8_t* mat, int K, int j0, int J, uint32_t rowmask,
+                          int slot_fixed, int e, const int* s_ids, float* s_D) {
+  const int lane = threadIdx.x & 63;
+  const int lpr = lanes_per_row(K), rpw = 64 / lpr, sr = lane / lpr, li = lane % lpr;
+  const int64_t rb = row_bytes(BITS, K);
+  const uint32_t* sb = (const uint32_t*)(mat + matrix_codes_bytes(BITS, d.H, K));
+  int jj[RD];
+  const uint8_t* rc[RD];
+  const uint32_t* rs[RD];
+#pragma unroll
+  for (int r = 0; r < RD; ++r) {
+    const int q = sr + rpw * r;
+    const bool ok = q < J && j0 + q < d.H;
+    jj[r] = ok ? q : -1;
+    rc[r] = ok ? mat + (int64_t)(j0 + q) * rb : nullptr;
+    rs[r] = ok ? sb + (int64_t)(j0 + q) * (K >> 6) : nullptr;
+  }
+  RowsQ<BITS, CPL, RD> Q;
+  load_rows<BITS, CPL, RD>(Q, rc, rs, K, (int)(rb >> 2), li, lpr);
+  XLane<BITS, CPL> xh, xl;
+  float out[RD];
+  for (int t = 0; t < d.T; ++t) {
+    if (!(rowmask >> t & 1u)) continue;
+    int slot = slot_fixed;
+    if (slot < 0)
+      for (int i = 0; i < d.k; ++i)
+        if (s_ids[t * d.k + i] == e) slot = i;
+    const int64_t aoff = ((int64_t)t * (d.k + 1) + slot) * d.imax;
+    prep_x<BITS, CPL>(xh, p.a_hi + aoff, K, li, lpr);
+    prep_x<BITS, CPL>(xl, p.a_lo + aoff, K, li, lpr);
+    dot_rows<BITS, CPL, RD, 2>(Q, xh, xl, out);
+#pragma unroll
+    for (int r = 0; r < RD; ++r) {
+      const float v = reduce_row(out[r], lpr);
+      if (jj[r] >= 0 && li == lpr - 1) s_D[(t * (d.k + 1) + slot) * J + jj[r]] = v;
     }
   }
-  topk_kernel<<<1, kThreads, 0, st>>>((const uint16_t*)(layer + c.L.gatevec), E, H, k, T, s.rms_eps, h_in, raw, rinv,
-                                      sg, ids, wts, units, masks, ids_out, w_out);
-  {  // gate/up, routed units then shared expert
-    const int rpb = rows_per_block_for(H, 4);
-    dim3 g(blocks_for(s.inter, rpb), max_units);
-    MOE_BITS_SWITCH(s.expert_bits, B,
-                    gateup_kernel<B><<<g, kThreads, 0, st>>>(layer, c.L.expert0, c.L.expert_stride, c.L.expert_up,
-                                                             s.inter, H, k, T, 0, rpb, h_in, rinv, ids, units, masks,
-                                                             a_hi, a_lo, imax));
-    dim3 gs(blocks_for(s.shared_inter, rpb), 1);
-    MOE_BITS_SWITCH(s.shared_bits, B,
-                    gateup_kernel<B><<<gs, kThreads, 0, st>>>(layer, c.L.shared, 0, c.L.shared_up, s.shared_inter, H,
-                                                              k, T, 1, rpb, h_in, rinv, ids, units, masks, a_hi, a_lo,
-                                                              imax));
+}
+
+template <int CPL, int RD>
+__global__ void __launch_bounds__(1024) down_kernel(Dims d, Ptrs p, int J) {
+  __shared__ float s_D[kMaxT * (kMaxTopK + 1) * 16];
+  __shared__ int s_ids[kMaxT * kMaxTopK];
+  __shared__ float s_w[kMaxT * kMaxTopK];
+  __shared__ float s_sg[kMaxT];
+  __shared__ int s_units[kMaxUnits + 1];
+  __shared__ uint32_t s_masks[kMaxUnits];
+  const int tid = threadIdx.x, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int j0 = blockIdx.x * J;
+  // routing of this call, staged once (parallel loads)
+  const int n_units = p.units[0];
+  for (int i = tid; i < d.T * d.k; i += blockDim.x) {
+    s_ids[i] = p.ids[i];
+    s_w[i] = p.wts[i];
   }
-  {  // down: routed, then shared + combine
-    const int rpb = rows_per_block_for(s.inter, 4);
-    dim3 g(blocks_for(H, rpb), max_units);
-    MOE_BITS_SWITCH(s.expert_bits, B,
-                    down_kernel<B><<<g, kThreads, 0, st>>>(layer, c.L.expert0, c.L.expert_stride, c.L.expert_down,
-                                                           s.inter, H, k, T, rpb, ids, units, masks, a_hi, a_lo, imax,
-                                                           dsum));
-    const int rps = rows_per_block_for(s.shared_inter, 2);
-    MOE_BITS_SWITCH(s.shared_bits, B,
-                    down_combine_kernel<B><<<blocks_for(H, rps), kThreads, 0, st>>>(
-                        layer, c.L.shared, c.L.shared_down, s.shared_inter, H, k, T, rps, h_in, wts, sg, a_hi, a_lo,
-                        imax, dsum, h_out));
+  for (int i = tid; i < d.T; i += blockDim.x) s_sg[i] = p.sg[i];
+  for (int i = tid; i < n_units; i += blockDim.x) {
+    s_units[i] = p.units[1 + i];
+    s_masks[i] = p.masks[i];
+  }
+  // residual inputs of this thread's first combine slot, loaded up front
+  float h0 = 0.f;
+  if (tid < d.T * J && j0 + tid % J < d.H) h0 = __uint_as_float((uint32_t)p.h_in[(int64_t)(tid / J) * d.H + j0 + tid % J] << 16);
+  __syncthreads();
+  const uint32_t all = d.T >= 32 ? 0xFFFFFFFFu : ((1u << d.T) - 1u);
+  for (int u = wave; u <= n_units; u += nw) {
+    if (u < n_units) {
+      const int e = s_units[u];
+      const uint8_t* mat = p.layer + d.off_e0 + (int64_t)e * d.e_stride + d.off_e_down;
+      MOE_BITS_CASES(d.ebits, B, down_unit<B, CPL, RD>(d, p, mat, d.I, j0, J, s_masks[u], -1, e, s_ids, s_D));
+    } else {
+      const uint8_t* mat = p.layer + d.off_shared + d.off_shared_down;
+      MOE_BITS_CASES(d.sbits, B, down_unit<B, CPL, RD>(d, p, mat, d.Is, j0, J, all, d.k, -1, s_ids, s_D));
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < d.T * J; idx += blockDim.x) {
+    const int t = idx / J, q = idx % J, j = j0 + q;
+    if (j >= d.H) continue;
+    float acc = 0.f;
+    for (int i = 0; i < d.k; ++i) acc = fmaf(s_w[t * d.k + i], s_D[(t * (d.k + 1) + i) * J + q], acc);
+    acc = fmaf(s_sg[t], s_D[(t * (d.k + 1) + d.k) * J + q], acc);
+    const float hv = idx == tid ? h0 : __uint_as_float((uint32_t)p.h_in[(int64_t)t * d.H + j] << 16);
+    const float out = hv + acc;
+    p.h_out[(int64_t)t * d.H + j] = (uint16_t)f32_to_bf16_rne(out);
+  }
+}
+
+// ---------------------------------------------------------------- launch
+struct LayerPlan {
+  Dims d;
+  int cpl_h, cpl_i;
+  int n_rt, n_st, tpu, g_grid;
+  int J, RD, d_grid, d_threads;
+};
+
+LayerPlan make_plan(const moe_shape_t& s, const moe_layer_layout_t& L, int T) {
+  LayerPlan P;
+  Dims& d = P.d;
+  d.H = s.hidden;
+  d.E = s.n_experts;
+  d.I = s.inter;
+  d.Is = s.shared_inter;
+  d.k = s.top_k;
+  d.T = T;
+  d.imax = s.inter > s.shared_inter ? s.inter : s.shared_inter;
+  d.rbits = s.router_bits;
+  d.ebits = s.expert_bits;
+  d.sbits = s.shared_bits;
+  d.eps = s.rms_eps;
+  d.off_router = L.router;
+  d.off_gatevec = L.gatevec;
+  d.off_shared = L.shared;
+  d.off_shared_up = L.shared_up;
+  d.off_shared_down = L.shared_down;
+  d.off_e0 = L.expert0;
+  d.e_stride = L.expert_stride;
+  d.off_e_up = L.expert_up;
+  d.off_e_down = L.expert_down;
+  P.cpl_h = chunks_per_lane(s.hidden);
+  P.cpl_i = chunks_per_lane(d.imax);
+  const int rpw_h = 64 / lanes_per_row(s.hidden);
+  const int R = P.cpl_h >= 2 ? 2 : 4;
+  P.n_rt = (d.E + R * rpw_h - 1) / (R * rpw_h);
+  P.n_st = (d.Is + (R / 2) * rpw_h - 1) / ((R / 2) * rpw_h);
+  P.tpu = (d.I + (R / 2) * rpw_h - 1) / ((R / 2) * rpw_h);
+  const int max_units = T * d.k < d.E ? T * d.k : d.E;
+  const int waves = max_units * P.tpu;
+  P.g_grid = (waves + 3) / 4;
+  if (P.g_grid > 2048) P.g_grid = 2048;
+  // down: J output rows per workgroup (about 256 workgroups), RD rows per lane
+  // group for the longest K, with RD * chunks <= 4 to bound registers
+  const int rpw_min = 64 / lanes_per_row(d.imax);  // rows per pass of the longest K
+  const int rd_max = 4 / P.cpl_i;
+  int J = pow2ceil((s.hidden + 255) / 256);
+  if (J < rpw_min) J = rpw_min;
+  if (J > rpw_min * rd_max) J = rpw_min * rd_max;
+  if (J > 16) J = 16;
+  P.J = J;
+  P.RD = (J + rpw_min - 1) / rpw_min;
+  P.d_grid = (s.hidden + P.J - 1) / P.J;
+  int nw = max_units + 1;
+  if (nw > 16) nw = 16;
+  P.d_threads = 64 * nw;
+  return P;
+}
+
+template <int CPL>
+void launch_route(const LayerPlan& P, const Ptrs& p, hipStream_t st) {
+  route_kernel<CPL><<<P.n_rt + P.n_st, 64, 0, st>>>(P.d, p, P.n_rt);
+}
+template <int CPL>
+void launch_expert(const LayerPlan& P, const Ptrs& p, hipStream_t st) {
+  expert_kernel<CPL><<<P.g_grid, 256, 0, st>>>(P.d, p, P.tpu);
+}
+template <int CPL, int RD>
+void launch_down(const LayerPlan& P, const Ptrs& p, hipStream_t st) {
+  down_kernel<CPL, RD><<<P.d_grid, P.d_threads, 0, st>>>(P.d, p, P.J);
+}
+
+#define MOE_CPL_CASES(cpl, C, ...)                     \
+  switch (cpl) {                                       \
+    case 1: { constexpr int C = 1; __VA_ARGS__; } break; \
+    case 2: { constexpr int C = 2; __VA_ARGS__; } break; \
+    default: { constexpr int C = 4; __VA_ARGS__; } break; \
+  }
+
+int32_t launch_layer(const LayerPlan& P, const WsMap& m, uint8_t* ws, const uint8_t* layer, const uint16_t* h_in,
+                     uint16_t* h_out, int32_t* ids_out, float* w_out, hipStream_t st) {
+  Ptrs p;
+  p.layer = layer;
+  p.h_in = h_in;
+  p.h_out = h_out;
+  p.ids_out = ids_out;
+  p.w_out = w_out;
+  p.raw = (float*)(ws + m.raw_logits);
+  p.rinv = (float*)(ws + m.rinv);
+  p.sg = (float*)(ws + m.sgate);
+  p.ids = (int*)(ws + m.ids);
+  p.wts = (float*)(ws + m.wts);
+  p.units = (int*)(ws + m.units);
+  p.masks = (uint32_t*)(ws + m.masks);
+  p.a_hi = (uint16_t*)(ws + m.a_hi);
+  p.a_lo = (uint16_t*)(ws + m.a_lo);
+  MOE_CPL_CASES(P.cpl_h, C, launch_route<C>(P, p, st));
+  MOE_CPL_CASES(P.cpl_h, C, launch_expert<C>(P, p, st));
+  // rows x chunks per lane <= 4 (make_plan)
+  switch (P.cpl_i * 8 + P.RD) {
+    case 8 + 1: launch_down<1, 1>(P, p, st); break;
+    case 8 + 2: launch_down<1, 2>(P, p, st); break;
+    case 8 + 4: launch_down<1, 4>(P, p, st); break;
+    case 16 + 1: launch_down<2, 1>(P, p, st); break;
+    case 16 + 2: launch_down<2, 2>(P, p, st); break;
+    default: launch_down<4, 1>(P, p, st); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(MOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -659,9 +559,11 @@ extern "C" int32_t moe_decode_layer(const moe_shape_t* shape, const void* layer_
   if (!layer_dev) return set_error(MOE_ERR_INVALID_ARG, "layer_dev is NULL");
   if ((uintptr_t)layer_dev % kAlign) return set_error(MOE_ERR_ALIGNMENT, "layer_dev must be 256-byte aligned");
   if (((uintptr_t)ids_dev % 4) || ((uintptr_t)w_dev % 4)) return set_error(MOE_ERR_ALIGNMENT, "ids/w must be 4-byte aligned");
-  LayerCall c{shape, {}, m, (uint8_t*)ws_dev, T};
-  layout_of(*shape, &c.L);
-  return launch_layer(c, (const uint8_t*)layer_dev, h_in_dev, h_out_dev, ids_dev, w_dev, (hipStream_t)stream);
+  moe_layer_layout_t L;
+  layout_of(*shape, &L);
+  const LayerPlan P = make_plan(*shape, L, T);
+  return launch_layer(P, m, (uint8_t*)ws_dev, (const uint8_t*)layer_dev, h_in_dev, h_out_dev, ids_dev, w_dev,
+                      (hipStream_t)stream);
 }
 
 extern "C" int32_t moe_decode_stack(const moe_shape_t* shape, const void* const* layers_host, int32_t n_layers,
@@ -680,8 +582,9 @@ extern "C" int32_t moe_decode_stack(const moe_shape_t* shape, const void* const*
   if (((uintptr_t)ids_dev % 4) || ((uintptr_t)w_dev % 4) || ((uintptr_t)h_trace_dev % 16))
     return set_error(MOE_ERR_ALIGNMENT, "ids/w must be 4-byte and h_trace 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
-  LayerCall c{shape, {}, m, (uint8_t*)ws_dev, T};
-  layout_of(*shape, &c.L);
+  moe_layer_layout_t L;
+  layout_of(*shape, &L);
+  const LayerPlan P = make_plan(*shape, L, T);
   const int64_t th = (int64_t)T * shape->hidden;
   const int64_t tk = (int64_t)T * shape->top_k;
   uint16_t* hb = (uint16_t*)((uint8_t*)ws_dev + m.hbuf);
@@ -695,8 +598,8 @@ extern "C" int32_t moe_decode_stack(const moe_shape_t* shape, const void* const*
     if (h_trace_dev) nxt = h_trace_dev + (l + 1) * th;
     else if (l == n_layers - 1) nxt = h_out_dev;
     else nxt = hb + (l & 1) * th;
-    rc = launch_layer(c, (const uint8_t*)layers_host[l], cur, nxt, ids_dev ? ids_dev + l * tk : nullptr,
-                      w_dev ? w_dev + l * tk : nullptr, st);
+    rc = launch_layer(P, m, (uint8_t*)ws_dev, (const uint8_t*)layers_host[l], cur, nxt,
+                      ids_dev ? ids_dev + l * tk : nullptr, w_dev ? w_dev + l * tk : nullptr, st);
     if (rc) return rc;
     cur = nxt;
   }

@@ -1,0 +1,584 @@
+// Wave-level building blocks of the dequantising matrix-vector products
+// (gfx950, wave64).
+//
+// Work unit: a chunk of 32 consecutive codes of one row (half a quantisation
+// group of 64, so one scale/bias pair applies). A row of K codes has K/32
+// chunks; `lpr` lanes (a power of two <= 64) share a row and lane `li` takes
+// chunks li, li + lpr, ... (at most CPL of them). The lanes' partial sums are
+// combined by a fixed butterfly, so every result is bitwise reproducible and
+// independent of how many rows or tokens a launch handles.
+//
+// Arithmetic per chunk: with x the 32 input values and q the codes,
+//   sum_j (q_j s + b) x_j = s * D + (b - 128 s) * X,
+//   D = sum_j (128 + q_j) x_j,  X = sum_j x_j.
+// For 2/3/4/6-bit codes, (128 + q) is exactly the bf16 whose mantissa holds q,
+// so two codes become one bf16 pair with a single mask-and-or and D is a chain
+// of v_dot2c_f32_bf16 (fp32 accumulation) against bf16 pairs of x. 8-bit
+// codes are split into two nibble planes, q = 16 hi + lo, each decoded the
+// same way: sum q x = D_lo + 16 D_hi - 2176 X. The flash-moe news page's reordered
+// dequantisation ("FMA-optimised dequant kernel") folds scale and bias into
+// the input; here they are applied once per half-group instead.
+#pragma once
+
+#include <climits>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace moe {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kMagic = 0x43004300u;  // bf16 pair (128, 128)
+constexpr uint32_t kOnes = 0x3F803F80u;   // bf16 pair (1, 1)
+constexpr int kDense = 16;                // "bits" of a dense bf16 matrix
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+__host__ __device__ __forceinline__ int pow2ceil(int v) {
+  int p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+// lanes sharing one row of K codes
+__host__ __device__ __forceinline__ int lanes_per_row(int k) {
+  const int n = pow2ceil(k / 32);
+  return n < 64 ? n : 64;
+}
+// chunks per lane
+__host__ __device__ __forceinline__ int chunks_per_lane(int k) {
+  const int lpr = lanes_per_row(k);
+  return (k / 32 + lpr - 1) / lpr;
+}
+
+__device__ __forceinline__ void load64B(const void* p, uint32_t (&w)[16]) {
+  const u32x4* q = (const u32x4*)p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 v = q[i];
+    w[4 * i] = v.x;
+    w[4 * i + 1] = v.y;
+    w[4 * i + 2] = v.z;
+    w[4 * i + 3] = v.w;
+  }
+}
+
+// bf16 pair (element a, element b) of 32 natural-order bf16 values held as 16 words
+template <int A, int B>
+__device__ __forceinline__ uint32_t pair_of(const uint32_t (&n)[16]) {
+  const uint32_t wa = n[A >> 1], wb = n[B >> 1];
+  const uint32_t lo = (A & 1) ? (wa >> 16) : (wa & 0xFFFFu);
+  const uint32_t hi = (B & 1) ? (wb & 0xFFFF0000u) : (wb << 16);
+  return lo | hi;
+}
+
+// Pair order expected by the unpackers: bits 4/6 pair codes (8d+i, 8d+i+4),
+// bits 2 pair codes (16d+i, 16d+i+8), bits 8 pair codes (4k+i, 4k+i+2),
+// a dense bf16 matrix uses natural order (3 bits: see tri_arrange).
+template <int BITS>
+__device__ __forceinline__ void arrange_pairs(const uint32_t (&n)[16], uint32_t (&o)[16]) {
+  if constexpr (BITS == 2) {
+#define MOE_P2(d, i) o[8 * d + i] = pair_of<16 * d + i, 16 * d + i + 8>(n);
+    MOE_P2(0, 0) MOE_P2(0, 1) MOE_P2(0, 2) MOE_P2(0, 3) MOE_P2(0, 4) MOE_P2(0, 5) MOE_P2(0, 6) MOE_P2(0, 7)
+    MOE_P2(1, 0) MOE_P2(1, 1) MOE_P2(1, 2) MOE_P2(1, 3) MOE_P2(1, 4) MOE_P2(1, 5) MOE_P2(1, 6) MOE_P2(1, 7)
+#undef MOE_P2
+  } else if constexpr (BITS == 3 || BITS == 4 || BITS == 6) {
+#define MOE_P4(d, i) o[4 * d + i] = pair_of<8 * d + i, 8 * d + i + 4>(n);
+    MOE_P4(0, 0) MOE_P4(0, 1) MOE_P4(0, 2) MOE_P4(0, 3) MOE_P4(1, 0) MOE_P4(1, 1) MOE_P4(1, 2) MOE_P4(1, 3)
+    MOE_P4(2, 0) MOE_P4(2, 1) MOE_P4(2, 2) MOE_P4(2, 3) MOE_P4(3, 0) MOE_P4(3, 1) MOE_P4(3, 2) MOE_P4(3, 3)
+#undef MOE_P4
+  } else if constexpr (BITS == 8) {
+#define MOE_P8(k) o[2 * k] = pair_of<4 * k, 4 * k + 2>(n); o[2 * k + 1] = pair_of<4 * k + 1, 4 * k + 3>(n);
+    MOE_P8(0) MOE_P8(1) MOE_P8(2) MOE_P8(3) MOE_P8(4) MOE_P8(5) MOE_P8(6) MOE_P8(7)
+#undef MOE_P8
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[i] = n[i];
+  }
+}
+
+__device__ __forceinline__ float sum16(const uint32_t (&n)[16]) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s = dot2(n[i], kOnes, s);
+  return s;
+}
+
+// 3-bit codes are decoded in pairs (slot s, slot s+5) of each of the 5 words a
+// chunk touches (25 pairs, 50 code positions); chunk c starts at position
+// R = 32c mod 10 of that window, so position p holds chunk code p - R, and
+// the x pair of a position outside the chunk is zero.
+template <int R, int W, int S>
+__device__ __forceinline__ uint32_t tri_x_pair(const uint32_t (&n)[16]) {
+  constexpr int a = 10 * W + S - R, b = 10 * W + S + 5 - R;
+  uint32_t lo = 0u, hi = 0u;
+  if constexpr (a >= 0 && a < 32) lo = (a & 1) ? (n[a >> 1] >> 16) : (n[a >> 1] & 0xFFFFu);
+  if constexpr (b >= 0 && b < 32) hi = (b & 1) ? (n[b >> 1] & 0xFFFF0000u) : (n[b >> 1] << 16);
+  return lo | hi;
+}
+template <int R>
+__device__ __forceinline__ void tri_arrange(const uint32_t (&n)[16], uint32_t* o) {
+#define MOE_TX(w) o[5 * w + 0] = tri_x_pair<R, w, 0>(n); o[5 * w + 1] = tri_x_pair<R, w, 1>(n); \
+  o[5 * w + 2] = tri_x_pair<R, w, 2>(n); o[5 * w + 3] = tri_x_pair<R, w, 3>(n); o[5 * w + 4] = tri_x_pair<R, w, 4>(n);
+  MOE_TX(0) MOE_TX(1) MOE_TX(2) MOE_TX(3) MOE_TX(4)
+#undef MOE_TX
+}
+
+template <int BITS>
+struct XWords {
+  static constexpr int N = BITS == 3 ? 25 : 16;
+};
+
+// Input operand of one lane: CPL chunks of arranged words, and chunk sums.
+template <int BITS, int CPL>
+struct XLane {
+  uint32_t w[CPL][XWords<BITS>::N];
+  float s[CPL];
+};
+
+// x from a bf16 vector [K] (natural order)
+template <int BITS, int CPL>
+__device__ __forceinline__ void prep_x(XLane<BITS, CPL>& x, const uint16_t* v, int K, int li, int lpr) {
+  const int nch = K >> 5;
+#pragma unroll
+  for (int m = 0; m < CPL; ++m) {
+    const int c = li + lpr * m;
+    uint32_t n[16];
+    if (c < nch) {
+      load64B(v + 32 * c, n);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) n[i] = 0u;
+    }
+    if constexpr (BITS == 3) {
+      switch ((2 * c) % 10) {
+        case 0: tri_arrange<0>(n, x.w[m]); break;
+        case 2: tri_arrange<2>(n, x.w[m]); break;
+        case 4: tri_arrange<4>(n, x.w[m]); break;
+        case 6: tri_arrange<6>(n, x.w[m]); break;
+        default: tri_arrange<8>(n, x.w[m]); break;
+      }
+    } else {
+      arrange_pairs<BITS>(n, x.w[m]);
+    }
+    x.s[m] = sum16(n);
+  }
+}
+
+// Sum of squares of the lane's x values (every element of its chunks once).
+template <int BITS, int CPL>
+__device__ __forceinline__ float sumsq(const XLane<BITS, CPL>& x) {
+  float a = 0.f;
+#pragma unroll
+  for (int m = 0; m < CPL; ++m)
+#pragma unroll
+    for (int i = 0; i < XWords<BITS>::N; ++i) a = dot2(x.w[m][i], x.w[m][i], a);
+  return a;
+}
+
+// ------------------------------------------------------------ code loading
+// Raw packed words of chunk c (codes 32c .. 32c+31) of one row; up to 8 words.
+template <int BITS>
+__device__ __forceinline__ void load_chunk(const uint8_t* row, int c, int row_words, uint32_t (&q)[8]) {
+  if constexpr (BITS == 2) {
+    const u32x2 v = *(const u32x2*)(row + 8 * c);
+    q[0] = v.x;
+    q[1] = v.y;
+  } else if constexpr (BITS == 4) {
+    const u32x4 v = *(const u32x4*)(row + 16 * c);
+    q[0] = v.x;
+    q[1] = v.y;
+    q[2] = v.z;
+    q[3] = v.w;
+  } else if constexpr (BITS == 6) {
+    const u32x2* p = (const u32x2*)(row + 24 * c);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const u32x2 v = p[i];
+      q[2 * i] = v.x;
+      q[2 * i + 1] = v.y;
+    }
+  } else if constexpr (BITS == 8) {
+    const u32x4* p = (const u32x4*)(row + 32 * c);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const u32x4 v = p[i];
+      q[4 * i] = v.x;
+      q[4 * i + 1] = v.y;
+      q[4 * i + 2] = v.z;
+      q[4 * i + 3] = v.w;
+    }
+  } else if constexpr (BITS == 3) {
+    // codes 32c.. start in word w0 = floor(32c/10) at code offset (32c mod 10);
+    // the chunk touches at most 5 words (clamped to the row)
+    const uint32_t* w = (const uint32_t*)row;
+    const int w0 = (32 * c) / 10;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const int wi = w0 + i < row_words ? w0 + i : row_words - 1;
+      q[i] = w[wi];
+    }
+  }
+}
+
+// Code pairs (bf16 128+q) of a chunk for bits 2/3/4/6, in the order arrange_pairs uses.
+template <int BITS>
+__device__ __forceinline__ void code_pairs(const uint32_t (&q)[8], uint32_t (&p)[XWords<BITS>::N]) {
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[4 * d + i] = ((q[d] >> (4 * i)) & 0x000F000Fu) | kMagic;
+  } else if constexpr (BITS == 6) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int d = 0; d < 2; ++d)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int sh = 2 * (4 * d + i) - 4;
+          const uint32_t hw = q[3 * u + 2];
+          const uint32_t hs = sh >= 0 ? (hw >> sh) : (hw << (-sh));
+          p[4 * (2 * u + d) + i] = (((q[3 * u + d] >> (4 * i)) & 0x000F000Fu) | kMagic) | (hs & 0x00300030u);
+        }
+  } else if constexpr (BITS == 2) {
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[8 * d + i] = ((q[d] >> (2 * i)) & 0x00030003u) | kMagic;
+  } else if constexpr (BITS == 3) {
+#pragma unroll
+    for (int w = 0; w < 5; ++w)
+#pragma unroll
+      for (int sl = 0; sl < 5; ++sl) {
+        const uint32_t t = q[w] >> (3 * sl);
+        p[5 * w + sl] = (t & 7u) | ((t << 1) & 0x70000u) | kMagic;
+      }
+  }
+}
+
+// 8-bit codes as two nibble planes: q = 16 hi + lo, each plane decoded into
+// bf16 pairs (128 + nibble) for codes (4k+i, 4k+i+2) of dword k.
+__device__ __forceinline__ void byte_pairs(const uint32_t (&q)[8], uint32_t (&plo)[16], uint32_t (&phi)[16]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      plo[2 * k + i] = ((q[k] >> (8 * i)) & 0x000F000Fu) | kMagic;
+      phi[2 * k + i] = ((q[k] >> (8 * i + 4)) & 0x000F000Fu) | kMagic;
+    }
+}
+
+// Partial sum of one chunk: s*D + b_eff*X, for NX inputs (1 = single, 2 = hi/lo split).
+template <int BITS, int NX>
+__device__ __forceinline__ float chunk_partial(const uint32_t (&q)[8], uint32_t sbw,
+                                               const uint32_t (&x0)[XWords<BITS>::N], float s0,
+                                               const uint32_t (&x1)[XWords<BITS>::N], float s1) {
+  const float s = bf16_lo_to_f32(sbw), b = bf16_hi_to_f32(sbw);
+  if constexpr (BITS == 8) {
+    // sum q x = D_lo + 16 D_hi - (128 + 16*128) X
+    uint32_t pl[16], ph[16];
+    byte_pairs(q, pl, ph);
+    float dl = 0.f, dh = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dl = dot2(pl[i], x0[i], dl);
+      dh = dot2(ph[i], x0[i], dh);
+    }
+    float sx = s0;
+    if constexpr (NX == 2) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        dl = dot2(pl[i], x1[i], dl);
+        dh = dot2(ph[i], x1[i], dh);
+      }
+      sx += s1;
+    }
+    return fmaf(s, fmaf(16.f, dh, dl), (b - 2176.f * s) * sx);
+  } else {
+    constexpr int NW = XWords<BITS>::N;
+    uint32_t p[NW];
+    code_pairs<BITS>(q, p);
+    float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      d0 = dot2(p[i], x0[i], d0);
+      if constexpr (NX == 2) d1 = dot2(p[i], x1[i], d1);
+    }
+    float d = d0, sx = s0;
+    if constexpr (NX == 2) {
+      d += d1;
+      sx += s1;
+    }
+    return fmaf(s, d, (b - 128.f * s) * sx);
+  }
+}
+
+// Dense bf16 row chunk: sum_j w_j x_j (natural pairs)
+__device__ __forceinline__ float dense_chunk(const uint32_t (&w)[16], const uint32_t (&x)[16]) {
+  float d = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) d = dot2(w[i], x[i], d);
+  return d;
+}
+
+// Codes of R rows for one lane (CPL chunks each), loaded before any arithmetic.
+template <int BITS, int CPL, int R>
+struct RowsQ {
+  uint32_t q[R][CPL][8];
+  uint32_t sb[R][CPL];
+};
+
+// rc[r]: first byte of row r's codes (nullptr = unused slot, result 0);
+// rs[r]: its scale/bias words. K columns, row_words = dwords per row.
+template <int BITS, int CPL, int R>
+__device__ __forceinline__ void load_rows(RowsQ<BITS, CPL, R>& Q, const uint8_t* const (&rc)[R],
+                                          const uint32_t* const (&rs)[R], int K, int row_words, int li, int lpr) {
+  const int nch = K >> 5;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = li + lpr * c;
+      const bool ok = rc[r] != nullptr && ch < nch;
+      if (ok) {
+        load_chunk<BITS>(rc[r], ch, row_words, Q.q[r][c]);
+        Q.sb[r][c] = rs[r][ch >> 1];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) Q.q[r][c][i] = 0u;
+        Q.sb[r][c] = 0u;  // scale 0, bias 0: contributes exactly 0
+      }
+    }
+}
+
+// Marks the packed words as redefined (no instruction is emitted): keeps the
+// compiler from hoisting the unpacking of every row out of a loop over token
+// rows, which would hold all decoded pairs live at once.
+template <int BITS, int CPL, int R>
+__device__ __forceinline__ void opaque(RowsQ<BITS, CPL, R>& Q) {
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(Q.q[r][c][i]));
+}
+
+template <int BITS, int CPL, int R, int NX>
+__device__ __forceinline__ void dot_rows(RowsQ<BITS, CPL, R>& Q, const XLane<BITS, CPL>& x0,
+                                         const XLane<BITS, CPL>& x1, float (&out)[R]) {
+  opaque(Q);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc += chunk_partial<BITS, NX>(Q.q[r][c], Q.sb[r][c], x0.w[c], x0.s[c], x1.w[c], x1.s[c]);
+    out[r] = acc;
+  }
+}
+
+// Dense bf16 rows (a bf16 router): 16 words per chunk.
+template <int CPL, int R>
+struct RowsD {
+  uint32_t w[R][CPL][16];
+};
+
+template <int CPL, int R>
+__device__ __forceinline__ void load_dense_rows(RowsD<CPL, R>& Q, const uint16_t* const (&rows)[R], int K, int li,
+                                                int lpr) {
+  const int nch = K >> 5;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = li + lpr * c;
+      if (rows[r] != nullptr && ch < nch) {
+        load64B(rows[r] + 32 * ch, Q.w[r][c]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Q.w[r][c][i] = 0u;
+      }
+    }
+}
+
+template <int CPL, int R>
+__device__ __forceinline__ void dot_dense_rows(RowsD<CPL, R>& Q, const XLane<kDense, CPL>& x, float (&out)[R]) {
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(Q.w[r][c][i]));
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc += dense_chunk(Q.w[r][c], x.w[c]);
+    out[r] = acc;
+  }
+}
+
+// ------------------------------------------------------ DPP wave reductions
+// GFX9 data-parallel-primitive lane moves (no LDS round trip):
+// quad_perm, row_half_mirror, row_mirror, row_bcast:15, row_bcast:31.
+constexpr int kDppXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+constexpr int kDppBcast15 = 0x142;
+constexpr int kDppBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f(float v, float old) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Sum over the lpr lanes of each row group (fixed tree). The group's last lane
+// (li == lpr - 1) holds the sum; for lpr <= 16 every lane of the group does.
+__device__ __forceinline__ float reduce_row(float v, int lpr) {
+  if (lpr > 1) v += dpp_f<kDppXor1>(v, 0.f);
+  if (lpr > 2) v += dpp_f<kDppXor2>(v, 0.f);
+  if (lpr > 4) v += dpp_f<kDppHalfMirror>(v, 0.f);
+  if (lpr > 8) v += dpp_f<kDppMirror>(v, 0.f);
+  if (lpr > 16) v += dpp_f<kDppBcast15, 0xA>(v, 0.f);
+  if (lpr > 32) v += dpp_f<kDppBcast31, 0xC>(v, 0.f);
+  return v;
+}
+
+// Wave-wide sum, returned to every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = reduce_row(v, 64);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Wave-wide maximum, returned to every lane.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v, -INFINITY));
+  v = fmaxf(v, dpp_f<kDppXor2>(v, -INFINITY));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v, -INFINITY));
+  v = fmaxf(v, dpp_f<kDppMirror>(v, -INFINITY));
+  v = fmaxf(v, dpp_f<kDppBcast15, 0xA>(v, -INFINITY));
+  v = fmaxf(v, dpp_f<kDppBcast31, 0xC>(v, -INFINITY));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// ------------------------------------------------------------------ top-k
+// Order-preserving integer key of a float (larger float -> larger key).
+__device__ __forceinline__ int fkey(float f) {
+  const int b = __float_as_int(f + 0.0f);  // -0 -> +0
+  return b >= 0 ? b : (b ^ 0x7FFFFFFF);
+}
+__device__ __forceinline__ float key_f(int k) { return __int_as_float(k >= 0 ? k : (k ^ 0x7FFFFFFF)); }
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i(int v, int old) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, false);
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+  v = max(v, dpp_i<kDppXor1>(v, INT_MIN));
+  v = max(v, dpp_i<kDppXor2>(v, INT_MIN));
+  v = max(v, dpp_i<kDppHalfMirror>(v, INT_MIN));
+  v = max(v, dpp_i<kDppMirror>(v, INT_MIN));
+  v = max(v, dpp_i<kDppBcast15, 0xA>(v, INT_MIN));
+  v = max(v, dpp_i<kDppBcast31, 0xC>(v, INT_MIN));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ int wave_min_i(int v) {
+  v = min(v, dpp_i<kDppXor1>(v, INT_MAX));
+  v = min(v, dpp_i<kDppXor2>(v, INT_MAX));
+  v = min(v, dpp_i<kDppHalfMirror>(v, INT_MAX));
+  v = min(v, dpp_i<kDppMirror>(v, INT_MAX));
+  v = min(v, dpp_i<kDppBcast15, 0xA>(v, INT_MAX));
+  v = min(v, dpp_i<kDppBcast31, 0xC>(v, INT_MAX));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Top-k of E logits (lane l holds e = l + 64 m), ties to the lower index,
+// descending; renormalised softmax weights over the k selected. All lanes end
+// with the same ids/w. E <= 512, k <= 16.
+// Each lane first sorts its M values (key descending, index ascending); each
+// round takes the wave maximum of the lanes' list heads; if several lanes hold
+// that key, the lowest index among them wins; the winner pops its head.
+__device__ __forceinline__ void wave_topk(const float* lam_src, const float* scale_src, int E, int k,
+                                          int (&ids)[kMaxTopK], float (&w)[kMaxTopK], float& scale_out) {
+  const int lane = threadIdx.x & 63;
+  constexpr int M = kMaxExperts / 64;
+  const float scale = *scale_src;
+  scale_out = scale;
+  int key[M], idx[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int e = lane + 64 * m;
+    key[m] = e < E ? fkey(scale * lam_src[e]) : INT_MIN;
+    idx[m] = e;
+  }
+  // sort the lane's list: key descending, index ascending (odd-even transposition)
+#pragma unroll
+  for (int pass = 0; pass < M; ++pass)
+#pragma unroll
+    for (int m = pass & 1; m + 1 < M; m += 2) {
+      const bool swap = key[m + 1] > key[m] || (key[m + 1] == key[m] && idx[m + 1] < idx[m]);
+      const int k0 = key[m], i0 = idx[m];
+      key[m] = swap ? key[m + 1] : k0;
+      idx[m] = swap ? idx[m + 1] : i0;
+      key[m + 1] = swap ? k0 : key[m + 1];
+      idx[m + 1] = swap ? i0 : idx[m + 1];
+    }
+  float sel[kMaxTopK];
+#pragma unroll
+  for (int i = 0; i < kMaxTopK; ++i) {
+    if (i < k) {
+      const int mx = wave_max_i(key[0]);
+      const unsigned long long b = __ballot(key[0] == mx);
+      int id;
+      if (__popcll(b) == 1) {
+        id = __builtin_amdgcn_readlane(idx[0], (int)__builtin_ctzll(b));
+      } else {
+        id = wave_min_i(key[0] == mx ? idx[0] : INT_MAX);
+      }
+      if (idx[0] == id) {  // the winner pops its head
+#pragma unroll
+        for (int m = 0; m + 1 < M; ++m) {
+          key[m] = key[m + 1];
+          idx[m] = idx[m + 1];
+        }
+        key[M - 1] = INT_MIN;
+        idx[M - 1] = INT_MAX;
+      }
+      sel[i] = key_f(mx);
+      ids[i] = id;
+    } else {
+      sel[i] = -INFINITY;
+      ids[i] = 0;
+    }
+  }
+  const float mx = sel[0];
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxTopK; ++i) {
+    w[i] = 0.f;
+    if (i < k) {  // uniform branch
+      w[i] = expf(sel[i] - mx);
+      sum += w[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kMaxTopK; ++i)
+    if (i < k) w[i] = w[i] / sum;
+}
+
+// Entry `lane` of a uniform array (lanes >= N get entry 0).
+template <typename V, int N>
+__device__ __forceinline__ V lane_pick(const V (&a)[N], int lane) {
+  V r = a[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) r = lane == i ? a[i] : r;
+  return r;
+}
+
+}  // namespace moe

@@ -19,8 +19,8 @@ namespace moe {
 constexpr int kGroup = 64;
 constexpr int kMaxT = 32;
 constexpr int kMaxTopK = 16;
-constexpr int kMaxExperts = 1024;
-constexpr int kMaxDim = 16384;
+constexpr int kMaxExperts = 512;
+constexpr int kMaxDim = 8192;
 constexpr int64_t kAlign = 256;
 
 MOE_HD inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }

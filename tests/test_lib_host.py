@@ -87,11 +87,13 @@ def test_workspace_bytes():
         ("group", 32, moe.MOE_ERR_UNSUPPORTED),
         ("group", 128, moe.MOE_ERR_UNSUPPORTED),
         ("hidden", 100, moe.MOE_ERR_UNSUPPORTED),
+        ("hidden", 16384, moe.MOE_ERR_UNSUPPORTED),
         ("inter", 0, moe.MOE_ERR_UNSUPPORTED),
         ("top_k", 0, moe.MOE_ERR_INVALID_ARG),
         ("top_k", 17, moe.MOE_ERR_INVALID_ARG),
         ("n_experts", 0, moe.MOE_ERR_INVALID_ARG),
         ("n_experts", 2000, moe.MOE_ERR_INVALID_ARG),
+        ("n_experts", 513, moe.MOE_ERR_INVALID_ARG),
         ("rms_eps", 0.0, moe.MOE_ERR_INVALID_ARG),
     ],
 )
