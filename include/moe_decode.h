@@ -166,7 +166,10 @@ int32_t moe_decode_layer(const moe_shape_t* shape, const void* layer_dev, int32_
 /*
  * A stack of n_layers MoE layers with distinct weights: h_0 = h_in,
  * h_{l+1} = bf16(layer_l(h_l)), h_out = h_{n_layers}. The host never waits
- * inside the stack.
+ * inside the stack. Each group of up to 64 layers runs as one kernel with one
+ * workgroup per compute unit whose workgroups wait on each other's results
+ * (bounded waits; see moe_stack_status); shapes it does not cover run as
+ * three kernels per layer, which give the same results bit for bit.
  *   layers_host : host array of n_layers device pointers to layer blocks
  *   ids_dev     : int32 [n_layers, T, k] or NULL; w_dev: float [n_layers, T, k] or NULL
  *   h_trace_dev : bf16 [n_layers + 1, T, H] (h_0 .. h_L) or NULL
@@ -175,6 +178,16 @@ int32_t moe_decode_layer(const moe_shape_t* shape, const void* layer_dev, int32_
 int32_t moe_decode_stack(const moe_shape_t* shape, const void* const* layers_host, int32_t n_layers, int32_t T,
                          const uint16_t* h_in_dev, uint16_t* h_out_dev, int32_t* ids_dev, float* w_dev,
                          uint16_t* h_trace_dev, void* ws_dev, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * Reads the status word the last moe_decode_stack call on this workspace
+ * left (waits for the stream first): 0 = every cross-workgroup wait was met;
+ * 1 = a wait timed out (about a second without progress, e.g. when other
+ * work kept part of the stack kernel's workgroups off the device), the call's
+ * outputs are then invalid. T must be the T of that call.
+ */
+int32_t moe_stack_status(const moe_shape_t* shape, int32_t T, const void* ws_dev, uint32_t* status_host,
+                         moe_stream_t stream);
 
 /* Message for the last failure on this thread ("" if none). Valid until the
  * thread's next call into the library. */

@@ -27,6 +27,7 @@ from ._lib import (  # noqa: F401
     moe_matrix_bytes,
     moe_pack_matrix,
     moe_shape_t,
+    moe_stack_status,
     moe_unpack_matrix,
     moe_validate_shape,
     moe_version,

@@ -91,6 +91,8 @@ def lib() -> ctypes.CDLL:
         L.moe_decode_stack.argtypes = [sp, ctypes.POINTER(c_vp), c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                        c_sz, c_vp]
         L.moe_decode_stack.restype = c_i32
+        L.moe_stack_status.argtypes = [sp, c_i32, c_vp, ctypes.POINTER(ctypes.c_uint32), c_vp]
+        L.moe_stack_status.restype = c_i32
         L.moe_last_error.argtypes = []
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_version.argtypes = []
@@ -188,6 +190,12 @@ def moe_decode_stack(shape: moe_shape_t, layers_dev: Sequence[int], T: int, h_in
     arr = (c_vp * len(layers_dev))(*[_p(p) for p in layers_dev])
     _check(lib().moe_decode_stack(ctypes.byref(shape), arr, len(layers_dev), T, _p(h_in_dev), _p(h_out_dev),
                                   _p(ids_dev), _p(w_dev), _p(h_trace_dev), _p(ws_dev), ws_bytes, _p(stream)))
+
+
+def moe_stack_status(shape: moe_shape_t, T: int, ws_dev: int, stream: int = 0) -> int:
+    v = ctypes.c_uint32(0)
+    _check(lib().moe_stack_status(ctypes.byref(shape), T, _p(ws_dev), ctypes.byref(v), _p(stream)))
+    return v.value
 
 
 def moe_last_error() -> str:

@@ -35,6 +35,7 @@
 // fixed order, and the arithmetic of one (token row, output) pair is the same
 // whatever T is and whichever rows share an expert.
 #include <cmath>
+#include <cstdlib>
 
 #include "gemv.h"
 
@@ -85,23 +86,33 @@ struct TaskRows {
   static constexpr int R = CPL >= 2 ? 2 : 4;  // rows loaded per lane group
 };
 
-// RMS factor and shared-expert gate of token row t (written once per call).
-// ss: sum of squares of the row (valid in the group's last lane).
-__device__ __forceinline__ void row_stats(const Dims& d, const Ptrs& p, int t, int li, int lpr, float ss) {
+// RMS factor and shared-expert gate of token row t (written once per call),
+// from the lane's arranged x chunks: ss = sum of squares, gate = gvec . h with
+// gvec arranged the same way (the stack kernel uses the same order).
+template <int BITS, int CPL>
+__device__ __forceinline__ void row_stats(const Dims& d, const Ptrs& p, int t, int li, int lpr, int sr,
+                                          const XLane<BITS, CPL>& x) {
   const uint16_t* gv = (const uint16_t*)(p.layer + d.off_gatevec);
-  const uint16_t* ht = p.h_in + (int64_t)t * d.H;
   const int nch = d.H >> 5;
   float gd = 0.f;
-  for (int c = li; c < nch; c += lpr) {
-    uint32_t hw[16], gw[16];
-    load64B(ht + 32 * c, hw);
-    load64B(gv + 32 * c, gw);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) gd = dot2(hw[i], gw[i], gd);
+  for (int m = 0; m < CPL; ++m) {
+    const int c = li + lpr * m;
+    uint32_t n[16];
+    if (c < nch) {
+      load64B(gv + 32 * c, n);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) n[i] = 0u;
+    }
+    uint32_t g[XWords<BITS>::N];
+    arrange_chunk<BITS>(n, c, g);
+#pragma unroll
+    for (int i = 0; i < XWords<BITS>::N; ++i) gd = dot2(x.w[m][i], g[i], gd);
   }
+  const float ss = reduce_row(sumsq(x), lpr);
   gd = reduce_row(gd, lpr);
-  const int lane = threadIdx.x & 63;
-  if (lane == lpr - 1) {
+  if (sr == 0 && li == lpr - 1) {
     const float r = rms_factor(ss, d.H, d.eps);
     p.rinv[t] = r;
     p.sg[t] = 1.0f / (1.0f + expf(-(r * gd)));
@@ -129,7 +140,7 @@ __device__ __forceinline__ void router_task(const Dims& d, const Ptrs& p, int ta
     load_dense_rows<CPL, R>(Q, rp, d.H, li, lpr);
     for (int t = 0; t < d.T; ++t) {
       prep_x<kDense, CPL>(x, p.h_in + (int64_t)t * d.H, d.H, li, lpr);
-      if (task == 0) row_stats(d, p, t, li, lpr, reduce_row(sumsq(x), lpr));
+      if (task == 0) row_stats<kDense, CPL>(d, p, t, li, lpr, sr, x);
       dot_dense_rows<CPL, R>(Q, x, out);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
@@ -153,7 +164,7 @@ __device__ __forceinline__ void router_task(const Dims& d, const Ptrs& p, int ta
     XLane<BITS, CPL> x;
     for (int t = 0; t < d.T; ++t) {
       prep_x<BITS, CPL>(x, p.h_in + (int64_t)t * d.H, d.H, li, lpr);
-      if (task == 0) row_stats(d, p, t, li, lpr, reduce_row(sumsq(x), lpr));
+      if (task == 0) row_stats<BITS, CPL>(d, p, t, li, lpr, sr, x);
       dot_rows<BITS, CPL, R, 1>(Q, x, x, out);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
@@ -260,13 +271,10 @@ __global__ void __launch_bounds__(256, 2) expert_kernel(Dims d, Ptrs p, int task
   __syncthreads();
   // routing of every token row (row t on wave t % 4)
   for (int t = wave; t < d.T; t += 4) {
-    int ids[kMaxTopK];
-    float w[kMaxTopK];
-    float r;
-    wave_topk(p.raw + (int64_t)t * d.E, p.rinv + t, d.E, d.k, ids, w, r);
+    int my_id;
+    float my_w, r;
+    wave_topk(p.raw + (int64_t)t * d.E, p.rinv + t, d.E, d.k, my_id, my_w, r);
     // lane i publishes entry i
-    const int my_id = lane_pick(ids, lane);
-    const float my_w = lane_pick(w, lane);
     if (lane < d.k) {
       s_ids[t * kMaxTopK + lane] = my_id;
       s_w[t * kMaxTopK + lane] = my_w;
@@ -592,6 +600,18 @@ extern "C" int32_t moe_decode_stack(const moe_shape_t* shape, const void* const*
     hipError_t e = hipMemcpyAsync(h_trace_dev, h_in_dev, th * 2, hipMemcpyDeviceToDevice, st);
     if (e != hipSuccess) return set_error(MOE_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
   }
+  // one persistent kernel per up to 64 layers when the shape allows it
+  // (MOE_STACK_KERNEL=0 selects the per-layer kernels, for comparison)
+  static const bool use_stack_kernel = [] {
+    const char* v = getenv("MOE_STACK_KERNEL");
+    return !(v && v[0] == '0');
+  }();
+  if (use_stack_kernel) {
+    rc = launch_stack_persistent(*shape, L, m, (uint8_t*)ws_dev, layers_host, n_layers, T, h_in_dev, h_out_dev,
+                                 ids_dev, w_dev, h_trace_dev, st);
+    if (rc != MOE_ERR_UNSUPPORTED) return rc;
+    clear_error();
+  }
   const uint16_t* cur = h_in_dev;
   for (int l = 0; l < n_layers; ++l) {
     uint16_t* nxt;
@@ -607,5 +627,20 @@ extern "C" int32_t moe_decode_stack(const moe_shape_t* shape, const void* const*
     hipError_t e = hipMemcpyAsync(h_out_dev, cur, th * 2, hipMemcpyDeviceToDevice, st);
     if (e != hipSuccess) return set_error(MOE_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
   }
+  return MOE_OK;
+}
+
+extern "C" int32_t moe_stack_status(const moe_shape_t* shape, int32_t T, const void* ws_dev, uint32_t* status_host,
+                                    moe_stream_t stream) {
+  clear_error();
+  int32_t rc = check_shape(shape);
+  if (rc) return rc;
+  if (T < 1 || T > kMaxT) return set_error(MOE_ERR_INVALID_ARG, "T %d not in [1, %d]", T, kMaxT);
+  if (!ws_dev || !status_host) return set_error(MOE_ERR_INVALID_ARG, "NULL workspace or status");
+  const WsMap m = ws_map(*shape, T);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(status_host, (const uint8_t*)ws_dev + m.status, 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return set_error(MOE_ERR_HIP, "status read failed: %s", hipGetErrorString(e));
   return MOE_OK;
 }

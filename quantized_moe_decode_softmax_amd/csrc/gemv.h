@@ -140,6 +140,22 @@ struct XLane {
   float s[CPL];
 };
 
+// Arranged words of chunk c from its 16 natural-order words.
+template <int BITS>
+__device__ __forceinline__ void arrange_chunk(const uint32_t (&n)[16], int c, uint32_t* o) {
+  if constexpr (BITS == 3) {
+    switch ((2 * c) % 10) {
+      case 0: tri_arrange<0>(n, o); break;
+      case 2: tri_arrange<2>(n, o); break;
+      case 4: tri_arrange<4>(n, o); break;
+      case 6: tri_arrange<6>(n, o); break;
+      default: tri_arrange<8>(n, o); break;
+    }
+  } else {
+    arrange_pairs<BITS>(n, *reinterpret_cast<uint32_t(*)[16]>(o));
+  }
+}
+
 // x from a bf16 vector [K] (natural order)
 template <int BITS, int CPL>
 __device__ __forceinline__ void prep_x(XLane<BITS, CPL>& x, const uint16_t* v, int K, int li, int lpr) {
@@ -498,25 +514,19 @@ __device__ __forceinline__ int wave_min_i(int v) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
-// Top-k of E logits (lane l holds e = l + 64 m), ties to the lower index,
-// descending; renormalised softmax weights over the k selected. All lanes end
-// with the same ids/w. E <= 512, k <= 16.
+// Top-k of E logits (lane l holds the key of e = l + 64 m, m < M; entries
+// with e >= E hold INT_MIN), ties to the lower index, descending; renormalised
+// softmax weights over the k selected. Lane i < k ends with the i-th selected
+// expert and its weight. E <= 64 M, k <= 16.
 // Each lane first sorts its M values (key descending, index ascending); each
 // round takes the wave maximum of the lanes' list heads; if several lanes hold
 // that key, the lowest index among them wins; the winner pops its head.
-__device__ __forceinline__ void wave_topk(const float* lam_src, const float* scale_src, int E, int k,
-                                          int (&ids)[kMaxTopK], float (&w)[kMaxTopK], float& scale_out) {
+template <int M>
+__device__ __forceinline__ void topk_select(int (&key)[M], int k, int& lane_id, float& lane_w) {
   const int lane = threadIdx.x & 63;
-  constexpr int M = kMaxExperts / 64;
-  const float scale = *scale_src;
-  scale_out = scale;
-  int key[M], idx[M];
+  int idx[M];
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int e = lane + 64 * m;
-    key[m] = e < E ? fkey(scale * lam_src[e]) : INT_MIN;
-    idx[m] = e;
-  }
+  for (int m = 0; m < M; ++m) idx[m] = lane + 64 * m;
   // sort the lane's list: key descending, index ascending (odd-even transposition)
 #pragma unroll
   for (int pass = 0; pass < M; ++pass)
@@ -529,9 +539,14 @@ __device__ __forceinline__ void wave_topk(const float* lam_src, const float* sca
       key[m + 1] = swap ? k0 : key[m + 1];
       idx[m + 1] = swap ? i0 : idx[m + 1];
     }
+  // k rounds of wave max; the selected logits are wave-uniform, lane i keeps
+  // round i's (id, logit) so no per-lane array is ever indexed by the lane
   float sel[kMaxTopK];
+  float my_sel = -INFINITY;
+  lane_id = 0;
 #pragma unroll
   for (int i = 0; i < kMaxTopK; ++i) {
+    sel[i] = -INFINITY;
     if (i < k) {
       const int mx = wave_max_i(key[0]);
       const unsigned long long b = __ballot(key[0] == mx);
@@ -551,34 +566,36 @@ __device__ __forceinline__ void wave_topk(const float* lam_src, const float* sca
         idx[M - 1] = INT_MAX;
       }
       sel[i] = key_f(mx);
-      ids[i] = id;
-    } else {
-      sel[i] = -INFINITY;
-      ids[i] = 0;
+      if (lane == i) {
+        lane_id = id;
+        my_sel = sel[i];
+      }
     }
   }
+  // renormalised softmax over the k selected logits, max first
   const float mx = sel[0];
   float sum = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxTopK; ++i) {
-    w[i] = 0.f;
-    if (i < k) {  // uniform branch
-      w[i] = expf(sel[i] - mx);
-      sum += w[i];
-    }
-  }
-#pragma unroll
   for (int i = 0; i < kMaxTopK; ++i)
-    if (i < k) w[i] = w[i] / sum;
+    if (i < k) sum += expf(sel[i] - mx);  // uniform branch
+  lane_w = lane < k ? expf(my_sel - mx) / sum : 0.f;
 }
 
-// Entry `lane` of a uniform array (lanes >= N get entry 0).
-template <typename V, int N>
-__device__ __forceinline__ V lane_pick(const V (&a)[N], int lane) {
-  V r = a[0];
+// Top-k of one token row on one wave: logits lam_src[0..E) scaled by
+// *scale_src (the RMS factor); lane i < k receives the i-th (id, weight).
+__device__ __forceinline__ void wave_topk(const float* lam_src, const float* scale_src, int E, int k, int& lane_id,
+                                          float& lane_w, float& scale_out) {
+  const int lane = threadIdx.x & 63;
+  constexpr int M = kMaxExperts / 64;
+  const float scale = *scale_src;
+  scale_out = scale;
+  int key[M];
 #pragma unroll
-  for (int i = 1; i < N; ++i) r = lane == i ? a[i] : r;
-  return r;
+  for (int m = 0; m < M; ++m) {
+    const int e = lane + 64 * m;
+    key[m] = e < E ? fkey(scale * lam_src[e]) : INT_MIN;
+  }
+  topk_select(key, k, lane_id, lane_w);
 }
 
 }  // namespace moe

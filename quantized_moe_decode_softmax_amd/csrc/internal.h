@@ -21,6 +21,7 @@ constexpr int kMaxT = 32;
 constexpr int kMaxTopK = 16;
 constexpr int kMaxExperts = 512;
 constexpr int kMaxDim = 8192;
+constexpr int kMaxLayersPerLaunch = 64;
 constexpr int64_t kAlign = 256;
 
 MOE_HD inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
@@ -51,8 +52,14 @@ struct WsMap {
   int64_t masks;        // uint32 [U]   rows using each unit
   int64_t a_hi;         // bf16  [T][k+1][Imax]  SwiGLU activations, high part
   int64_t a_lo;         // bf16  [T][k+1][Imax]  low part: a = hi + lo to 16 significant bits
-  int64_t dsum;         // float [T][k][H] routed down projections per (row, rank)
   int64_t hbuf;         // bf16  [2][T][H] ping-pong for stacks
+  // stack kernel exchange buffers: 64-bit words = 32-bit payload | epoch << 32
+  int64_t tg_h;         // u64 [T][H/2]       hidden state, two bf16 per word
+  int64_t tg_logit;     // u64 [T][E]         raw router dot products
+  int64_t tg_rs;        // u64 [T][2]         RMS factor, shared-expert gate
+  int64_t tg_a;         // u64 [T][k+1][Imax] activations, bf16 hi | bf16 lo << 16
+  int64_t status;       // u32 [64]           word 0: nonzero after a timed-out wait
+  int64_t tg_end;       // end of the region the stack kernel clears per call
   int64_t total;
 };
 
@@ -63,6 +70,13 @@ int32_t set_error(int32_t code, const char* fmt, ...);
 void clear_error();
 
 int32_t check_shape(const moe_shape_t* s);
+
+// Stack decode with the persistent kernel (persist.hip). MOE_ERR_UNSUPPORTED,
+// with nothing launched, for shapes it does not handle.
+struct WsMap;
+int32_t launch_stack_persistent(const moe_shape_t& s, const moe_layer_layout_t& L, const WsMap& m, uint8_t* ws,
+                                const void* const* layers, int n_layers, int T, const uint16_t* h_in, uint16_t* h_out,
+                                int32_t* ids_out, float* w_out, uint16_t* h_trace_out, moe_stream_t st);
 void layout_of(const moe_shape_t& s, moe_layer_layout_t* out);
 
 }  // namespace moe

@@ -36,6 +36,8 @@ class DeviceStack:
         ]
         self.ws_bytes = L.moe_workspace_bytes(self.shape, t_max)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        # read the stack kernel's status word after every stack call (waits for the stream)
+        self.check_status = False
         if seed is not None:
             for i, buf in enumerate(self.layers):
                 L.moe_generate_layer(self.shape, seed, i, buf.data_ptr(), _stream())
@@ -71,7 +73,15 @@ class DeviceStack:
         L.moe_decode_stack(self.shape, [self.layers[i].data_ptr() for i in sel], T, h.data_ptr(), out.data_ptr(),
                            None if ids is None else ids.data_ptr(), None if w is None else w.data_ptr(),
                            None if tr is None else tr.data_ptr(), self.ws.data_ptr(), self.ws_bytes, _stream())
+        if self.check_status:
+            st = self.status(T)
+            if st != 0:
+                raise RuntimeError(f"moe_decode_stack: a cross-workgroup wait timed out (status {st})")
         return out, ids, w, tr
+
+    def status(self, T: int) -> int:
+        """Status word of the last stack call with T rows (0 = every wait was met)."""
+        return L.moe_stack_status(self.shape, T, self.ws.data_ptr(), _stream())
 
 
 def bf16_bits(t: torch.Tensor):

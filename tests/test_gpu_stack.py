@@ -75,6 +75,7 @@ def a3b():
     w = WORKLOADS["a3b"]
     log(f"[a3b] generating {w.n_layers} layers")
     ds = DeviceStack.from_workload(w, t_max=8)
+    ds.check_status = True
     torch.cuda.synchronize()
     yield ds
     del ds
@@ -93,8 +94,11 @@ def test_a3b_stack_40_layers_T1(a3b):
     assert drift < 0.1
 
 
-def test_a3b_stack_equals_layer_calls_and_is_deterministic(a3b):
-    x = a3b.rows(1001, 2)
+@pytest.mark.parametrize("T", [1, 2, 7])
+def test_a3b_stack_equals_layer_calls_and_is_deterministic(a3b, T):
+    """The stack call (one persistent kernel) and 40 chained one-layer calls
+    (three kernels each) compute every value in the same order: bitwise equal."""
+    x = a3b.rows(1001 + T, T)
     out, ids, w, tr = a3b.stack(x, trace=True)
     out2, ids2, w2, _ = a3b.stack(x)
     h = x
@@ -133,6 +137,7 @@ def test_a17b_stack_60_layers():
     w = WORKLOADS["a17b"]
     t0 = time.time()
     ds = DeviceStack.from_workload(w)
+    ds.check_status = True
     torch.cuda.synchronize()
     log(f"[a17b] generated 60 layers ({60 * ds.layout['total_bytes'] / 1e9:.1f} GB) in {time.time() - t0:.1f}s")
     x = ds.rows(1000, 1)

@@ -141,6 +141,12 @@ def test_decode_argument_errors_return_before_launch():
         moe.moe_decode_stack(s, [A * 16, 0], 1, A * 2, A * 4, None, None, None, A * 32, ws)
     assert e.value.code == moe.MOE_ERR_INVALID_ARG
     with pytest.raises(moe.MoeError) as e:
+        moe.moe_stack_status(s, 2, 0)
+    assert e.value.code == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_stack_status(s, 33, A * 32)
+    assert e.value.code == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as e:
         moe.moe_generate_layer(shape_of("tiny", expert_bits=5), 0, 0, A * 16)
     assert e.value.code == moe.MOE_ERR_UNSUPPORTED
     with pytest.raises(moe.MoeError) as e:
