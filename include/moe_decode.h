@@ -81,13 +81,20 @@ typedef struct moe_shape {
  *   (pad)  : to a multiple of 256 bytes
  * Codes inside a row (code j = column j):
  *   bits 2, 4, 8 : dense, LSB first: code j at bit offset bits*j of the row.
- *   bits 6       : units of 16 codes in 3 dwords. Unit u holds codes
- *                  16u..16u+15 (local index c = 0..15). dword 0 holds the low
- *                  4 bits of c = 0..7 at bit 4c, dword 1 those of c = 8..15 at
- *                  bit 4(c-8); dword 2 holds the high 2 bits: for c = 8d + i +
- *                  4s (d, s in {0,1}, i in 0..3) at bit 2(4d + i) + 16s.
- *   bits 3       : 10 codes per dword, code j in dword j/10 at bit 3(j%10);
- *                  bits 30-31 zero; each row padded to whole dwords with zero.
+ *   bits 6       : units of 16 codes in 3 dwords A, B, C. Unit u holds
+ *                  codes 16u..16u+15; local code c = j + 8h (h in {0,1},
+ *                  j in 0..7) lives in bits 16h..16h+15 of the dwords, at
+ *                  these offsets within that half: j = 0, 1: A bit 6j;
+ *                  j = 3, 4: B bit 6(j-3); j = 6, 7: C bit 6(j-6) (all 6
+ *                  bits); j = 2: low 4 bits at A bit 12, high 2 bits at C
+ *                  bit 12; j = 5: low 4 bits at B bit 12, high 2 bits at C
+ *                  bit 14. (Codes c and c+8 share bit positions, so one mask
+ *                  extracts both halves of a decode pair.)
+ *   bits 3       : 10 codes per dword, code j in dword j/10; with
+ *                  l = j%10 at bit 3l for l < 5 and at bit 16 + 3(l-5) for
+ *                  l >= 5 (codes l and l+5 share bit positions in the two
+ *                  halves); bits 15 and 31 zero; each row padded to whole
+ *                  dwords with zero.
  * row_bytes = cols*bits/8 for bits 2/4/6/8, 4*ceil(cols/10) for bits 3.
  */
 int64_t moe_matrix_bytes(int32_t bits, int32_t rows, int32_t cols);

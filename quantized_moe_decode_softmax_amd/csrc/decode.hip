@@ -80,6 +80,35 @@ __device__ __forceinline__ void store_a(const Dims& d, const Ptrs& p, int t, int
   p.a_lo[idx] = (uint16_t)f32_to_bf16_rne(a - __uint_as_float(hb));
 }
 
+// Down-projection inputs: hi and lo halves of the activation vector [K] as
+// arranged words, with the same words and sums as the stack kernel builds.
+template <int BITS, int CPL>
+__device__ __forceinline__ void prep_split(XLane<BITS, CPL>& xh, XLane<BITS, CPL>& xl, const uint16_t* hi,
+                                           const uint16_t* lo, int K, int li, int lpr) {
+  const int nch = K >> 5;
+#pragma unroll
+  for (int m = 0; m < CPL; ++m) {
+    const int c = li + lpr * m;
+    uint32_t w[32];
+    if (c < nch) {
+      uint32_t nh[16], nl[16];
+      load64B(hi + 32 * c, nh);
+      load64B(lo + 32 * c, nl);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        w[2 * i] = __builtin_amdgcn_perm(nl[i], nh[i], 0x05040100u);
+        w[2 * i + 1] = __builtin_amdgcn_perm(nl[i], nh[i], 0x07060302u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) w[i] = 0u;
+    }
+    split_arrange<BITS>(w, c, xh.w[m], xl.w[m]);
+    xh.s[m] = sum_words<XWords<BITS>::N>(xh.w[m]);
+    xl.s[m] = sum_words<XWords<BITS>::N>(xl.w[m]);
+  }
+}
+
 // rows per lane group of one wave task, by chunks per lane
 template <int CPL>
 struct TaskRows {
@@ -362,8 +391,7 @@ __device__ __forceinline__ void down_unit(const Dims& d, const Ptrs& p, const ui
       for (int i = 0; i < d.k; ++i)
         if (s_ids[t * d.k + i] == e) slot = i;
     const int64_t aoff = ((int64_t)t * (d.k + 1) + slot) * d.imax;
-    prep_x<BITS, CPL>(xh, p.a_hi + aoff, K, li, lpr);
-    prep_x<BITS, CPL>(xl, p.a_lo + aoff, K, li, lpr);
+    prep_split<BITS, CPL>(xh, xl, p.a_hi + aoff, p.a_lo + aoff, K, li, lpr);
     dot_rows<BITS, CPL, RD, 2>(Q, xh, xl, out);
 #pragma unroll
     for (int r = 0; r < RD; ++r) {

@@ -39,6 +39,65 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// Fused decode + dot of one bf16 code pair: acc += dot2(((a >> SH) & m) | mag,
+// x), i.e. v_lshrrev + v_and_or_b32 + v_dot2c_f32_bf16 in one block, so the
+// decoded pair lives in one temporary. m comes from an SGPR and mag from a
+// VGPR: this architecture reads one scalar operand per instruction and VOP3
+// takes no literal (left to itself the compiler emits an AND and an OR with
+// literals, and schedules decodes far ahead of their use).
+template <int SH>
+__device__ __forceinline__ void dq_dot(float& acc, uint32_t a, uint32_t m, uint32_t mag, uint32_t x) {
+  uint32_t t;
+  if constexpr (SH == 0) {
+    asm("v_and_or_b32 %1, %2, %3, %4\n\tv_dot2c_f32_bf16 %0, %1, %5"
+        : "+v"(acc), "=&v"(t)
+        : "v"(a), "s"(m), "v"(mag), "v"(x));
+  } else {
+    asm("v_lshrrev_b32 %1, %6, %2\n\tv_and_or_b32 %1, %1, %3, %4\n\tv_dot2c_f32_bf16 %0, %1, %5"
+        : "+v"(acc), "=&v"(t)
+        : "v"(a), "s"(m), "v"(mag), "v"(x), "i"(SH));
+  }
+}
+// Same pair against two inputs (acc0 += p . x0, acc1 += p . x1).
+template <int SH>
+__device__ __forceinline__ void dq_dot2(float& acc0, float& acc1, uint32_t a, uint32_t m, uint32_t mag, uint32_t x0,
+                                        uint32_t x1) {
+  uint32_t t;
+  if constexpr (SH == 0) {
+    asm("v_and_or_b32 %2, %3, %4, %5\n\tv_dot2c_f32_bf16 %0, %2, %6\n\tv_dot2c_f32_bf16 %1, %2, %7"
+        : "+v"(acc0), "+v"(acc1), "=&v"(t)
+        : "v"(a), "s"(m), "v"(mag), "v"(x0), "v"(x1));
+  } else {
+    asm("v_lshrrev_b32 %2, %8, %3\n\tv_and_or_b32 %2, %2, %4, %5\n\tv_dot2c_f32_bf16 %0, %2, %6\n\t"
+        "v_dot2c_f32_bf16 %1, %2, %7"
+        : "+v"(acc0), "+v"(acc1), "=&v"(t)
+        : "v"(a), "s"(m), "v"(mag), "v"(x0), "v"(x1), "i"(SH));
+  }
+}
+// acc += dot2(p, x) as v_dot2c_f32_bf16 (the opcode of the blocks above, so
+// the accumulator chain only ever feeds the same DOT opcode as its SrcC).
+__device__ __forceinline__ void dot2c(float& acc, uint32_t p, uint32_t x) {
+  asm("v_dot2c_f32_bf16 %0, %1, %2" : "+v"(acc) : "v"(p), "v"(x));
+}
+// A DOT result read by another VALU opcode (or as a DOT's A/B source) needs 3
+// wait states, which the compiler cannot see through the asm blocks that
+// wrote it: every accumulator chain ends in this fence before ordinary code
+// reads it.
+__device__ __forceinline__ void dot_fence(float& a) { asm volatile("s_nop 2" : "+v"(a)); }
+__device__ __forceinline__ void dot_fence(float& a, float& b) { asm volatile("s_nop 2" : "+v"(a), "+v"(b)); }
+
+// 6-bit split pair: low nibbles at bit SA of a, high 2 bits at bit SC of c
+// (moved to bits 4-5): ((a >> SA) & 0x000F000F | mag) | ((c >> (SC - 4)) & 0x00300030).
+template <int SA, int SCM4>
+__device__ __forceinline__ uint32_t split6(uint32_t a, uint32_t c, uint32_t m4, uint32_t m2, uint32_t mag) {
+  uint32_t t, u;
+  asm("v_lshrrev_b32 %0, %5, %2\n\tv_and_or_b32 %0, %0, %3, %4\n\tv_lshrrev_b32 %1, %7, %6\n\t"
+      "v_and_or_b32 %0, %1, %8, %0"
+      : "=&v"(t), "=&v"(u)
+      : "v"(a), "s"(m4), "v"(mag), "i"(SA), "v"(c), "i"(SCM4), "s"(m2));
+  return t;
+}
+
 __host__ __device__ __forceinline__ int pow2ceil(int v) {
   int p = 1;
   while (p < v) p <<= 1;
@@ -76,9 +135,10 @@ __device__ __forceinline__ uint32_t pair_of(const uint32_t (&n)[16]) {
   return lo | hi;
 }
 
-// Pair order expected by the unpackers: bits 4/6 pair codes (8d+i, 8d+i+4),
-// bits 2 pair codes (16d+i, 16d+i+8), bits 8 pair codes (4k+i, 4k+i+2),
-// a dense bf16 matrix uses natural order (3 bits: see tri_arrange).
+// Pair order expected by the unpackers: bits 4 pair codes (8d+i, 8d+i+4),
+// bits 6 pair codes (16u+j, 16u+j+8), bits 2 pair codes (16d+i, 16d+i+8),
+// bits 8 pair codes (4k+i, 4k+i+2), a dense bf16 matrix uses natural order
+// (3 bits: see tri_arrange).
 template <int BITS>
 __device__ __forceinline__ void arrange_pairs(const uint32_t (&n)[16], uint32_t (&o)[16]) {
   if constexpr (BITS == 2) {
@@ -86,7 +146,12 @@ __device__ __forceinline__ void arrange_pairs(const uint32_t (&n)[16], uint32_t 
     MOE_P2(0, 0) MOE_P2(0, 1) MOE_P2(0, 2) MOE_P2(0, 3) MOE_P2(0, 4) MOE_P2(0, 5) MOE_P2(0, 6) MOE_P2(0, 7)
     MOE_P2(1, 0) MOE_P2(1, 1) MOE_P2(1, 2) MOE_P2(1, 3) MOE_P2(1, 4) MOE_P2(1, 5) MOE_P2(1, 6) MOE_P2(1, 7)
 #undef MOE_P2
-  } else if constexpr (BITS == 3 || BITS == 4 || BITS == 6) {
+  } else if constexpr (BITS == 6) {
+#define MOE_P6(u, j) o[8 * u + j] = pair_of<16 * u + j, 16 * u + j + 8>(n);
+    MOE_P6(0, 0) MOE_P6(0, 1) MOE_P6(0, 2) MOE_P6(0, 3) MOE_P6(0, 4) MOE_P6(0, 5) MOE_P6(0, 6) MOE_P6(0, 7)
+    MOE_P6(1, 0) MOE_P6(1, 1) MOE_P6(1, 2) MOE_P6(1, 3) MOE_P6(1, 4) MOE_P6(1, 5) MOE_P6(1, 6) MOE_P6(1, 7)
+#undef MOE_P6
+  } else if constexpr (BITS == 3 || BITS == 4) {
 #define MOE_P4(d, i) o[4 * d + i] = pair_of<8 * d + i, 8 * d + i + 4>(n);
     MOE_P4(0, 0) MOE_P4(0, 1) MOE_P4(0, 2) MOE_P4(0, 3) MOE_P4(1, 0) MOE_P4(1, 1) MOE_P4(1, 2) MOE_P4(1, 3)
     MOE_P4(2, 0) MOE_P4(2, 1) MOE_P4(2, 2) MOE_P4(2, 3) MOE_P4(3, 0) MOE_P4(3, 1) MOE_P4(3, 2) MOE_P4(3, 3)
@@ -101,11 +166,32 @@ __device__ __forceinline__ void arrange_pairs(const uint32_t (&n)[16], uint32_t 
   }
 }
 
-__device__ __forceinline__ float sum16(const uint32_t (&n)[16]) {
+// Sum of the N bf16 pairs of w (a chunk in natural or arranged order).
+template <int N>
+__device__ __forceinline__ float sum_words(const uint32_t* w) {
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) s = dot2(n[i], kOnes, s);
+  for (int i = 0; i < N; ++i) s = dot2(w[i], kOnes, s);
   return s;
+}
+
+// Element indices (a, b) of arranged pair word i, for the orders above
+// (bits 3 excepted: see tri_arrange).
+template <int BITS>
+__host__ __device__ constexpr int pair_a(int i) {
+  return BITS == 2 ? 16 * (i / 8) + i % 8
+       : BITS == 4 ? 8 * (i / 4) + i % 4
+       : BITS == 6 ? 16 * (i / 8) + i % 8
+       : BITS == 8 ? 4 * (i / 2) + i % 2
+       : 2 * i;
+}
+template <int BITS>
+__host__ __device__ constexpr int pair_b(int i) {
+  return BITS == 2 ? pair_a<BITS>(i) + 8
+       : BITS == 4 ? pair_a<BITS>(i) + 4
+       : BITS == 6 ? pair_a<BITS>(i) + 8
+       : BITS == 8 ? pair_a<BITS>(i) + 2
+       : 2 * i + 1;
 }
 
 // 3-bit codes are decoded in pairs (slot s, slot s+5) of each of the 5 words a
@@ -181,7 +267,29 @@ __device__ __forceinline__ void prep_x(XLane<BITS, CPL>& x, const uint16_t* v, i
     } else {
       arrange_pairs<BITS>(n, x.w[m]);
     }
-    x.s[m] = sum16(n);
+    x.s[m] = sum_words<XWords<BITS>::N>(x.w[m]);
+  }
+}
+
+// Arranged hi and lo words of one chunk from 32 words w[e] = bf16 hi of element
+// e | bf16 lo << 16: one byte permute per word (3 bits via natural words).
+template <int BITS>
+__device__ __forceinline__ void split_arrange(const uint32_t (&w)[32], int c, uint32_t* xh, uint32_t* xl) {
+  if constexpr (BITS == 3) {
+    uint32_t hn[16], ln[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      hn[i] = __builtin_amdgcn_perm(w[2 * i + 1], w[2 * i], 0x05040100u);
+      ln[i] = __builtin_amdgcn_perm(w[2 * i + 1], w[2 * i], 0x07060302u);
+    }
+    arrange_chunk<3>(hn, c, xh);
+    arrange_chunk<3>(ln, c, xl);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      xh[i] = __builtin_amdgcn_perm(w[pair_b<BITS>(i)], w[pair_a<BITS>(i)], 0x05040100u);
+      xl[i] = __builtin_amdgcn_perm(w[pair_b<BITS>(i)], w[pair_a<BITS>(i)], 0x07060302u);
+    }
   }
 }
 
@@ -241,52 +349,97 @@ __device__ __forceinline__ void load_chunk(const uint8_t* row, int c, int row_wo
   }
 }
 
-// Code pairs (bf16 128+q) of a chunk for bits 2/3/4/6, in the order arrange_pairs uses.
-template <int BITS>
-__device__ __forceinline__ void code_pairs(const uint32_t (&q)[8], uint32_t (&p)[XWords<BITS>::N]) {
-  if constexpr (BITS == 4) {
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[4 * d + i] = ((q[d] >> (4 * i)) & 0x000F000Fu) | kMagic;
-  } else if constexpr (BITS == 6) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int d = 0; d < 2; ++d)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int sh = 2 * (4 * d + i) - 4;
-          const uint32_t hw = q[3 * u + 2];
-          const uint32_t hs = sh >= 0 ? (hw >> sh) : (hw << (-sh));
-          p[4 * (2 * u + d) + i] = (((q[3 * u + d] >> (4 * i)) & 0x000F000Fu) | kMagic) | (hs & 0x00300030u);
-        }
-  } else if constexpr (BITS == 2) {
-#pragma unroll
-    for (int d = 0; d < 2; ++d)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p[8 * d + i] = ((q[d] >> (2 * i)) & 0x00030003u) | kMagic;
-  } else if constexpr (BITS == 3) {
-#pragma unroll
-    for (int w = 0; w < 5; ++w)
-#pragma unroll
-      for (int sl = 0; sl < 5; ++sl) {
-        const uint32_t t = q[w] >> (3 * sl);
-        p[5 * w + sl] = (t & 7u) | ((t << 1) & 0x70000u) | kMagic;
-      }
-  }
+// Masks of the code fields in both bf16 halves
+constexpr uint32_t kM2 = 0x00030003u, kM3 = 0x00070007u, kM4 = 0x000F000Fu, kM6 = 0x003F003Fu, kM6H = 0x00300030u;
+
+// Sums over one chunk of (128 + q) x for the code pairs in the order
+// arrange_pairs uses: d0 against x0, d1 against x1 (NX = 2).
+template <int BITS, int NX, int SH>
+__device__ __forceinline__ void pair_dot(float& d0, float& d1, uint32_t a, uint32_t m, uint32_t mag, uint32_t x0,
+                                         uint32_t x1) {
+  if constexpr (NX == 2) dq_dot2<SH>(d0, d1, a, m, mag, x0, x1);
+  else dq_dot<SH>(d0, a, m, mag, x0);
+}
+template <int NX>
+__device__ __forceinline__ void word_dot(float& d0, float& d1, uint32_t p, uint32_t x0, uint32_t x1) {
+  dot2c(d0, p, x0);
+  if constexpr (NX == 2) dot2c(d1, p, x1);
 }
 
-// 8-bit codes as two nibble planes: q = 16 hi + lo, each plane decoded into
-// bf16 pairs (128 + nibble) for codes (4k+i, 4k+i+2) of dword k.
-__device__ __forceinline__ void byte_pairs(const uint32_t (&q)[8], uint32_t (&plo)[16], uint32_t (&phi)[16]) {
+template <int BITS, int NX>
+__device__ __forceinline__ void code_dots(const uint32_t (&q)[8], const uint32_t (&x0)[XWords<BITS>::N],
+                                          const uint32_t (&x1)[XWords<BITS>::N], float& d0, float& d1) {
+  const uint32_t mag = kMagic;
+  if constexpr (BITS == 4) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k)
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      plo[2 * k + i] = ((q[k] >> (8 * i)) & 0x000F000Fu) | kMagic;
-      phi[2 * k + i] = ((q[k] >> (8 * i + 4)) & 0x000F000Fu) | kMagic;
+    for (int d = 0; d < 4; ++d) {
+      pair_dot<4, NX, 0>(d0, d1, q[d], kM4, mag, x0[4 * d + 0], x1[4 * d + 0]);
+      pair_dot<4, NX, 4>(d0, d1, q[d], kM4, mag, x0[4 * d + 1], x1[4 * d + 1]);
+      pair_dot<4, NX, 8>(d0, d1, q[d], kM4, mag, x0[4 * d + 2], x1[4 * d + 2]);
+      pair_dot<4, NX, 12>(d0, d1, q[d], kM4, mag, x0[4 * d + 3], x1[4 * d + 3]);
     }
+  } else if constexpr (BITS == 6) {
+    // unit u: dwords A, B, C; pair j holds codes (j, j + 8) of the unit
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t A = q[3 * u], B = q[3 * u + 1], C = q[3 * u + 2];
+      const int o = 8 * u;
+      pair_dot<6, NX, 0>(d0, d1, A, kM6, mag, x0[o + 0], x1[o + 0]);
+      pair_dot<6, NX, 6>(d0, d1, A, kM6, mag, x0[o + 1], x1[o + 1]);
+      word_dot<NX>(d0, d1, split6<12, 8>(A, C, kM4, kM6H, mag), x0[o + 2], x1[o + 2]);
+      pair_dot<6, NX, 0>(d0, d1, B, kM6, mag, x0[o + 3], x1[o + 3]);
+      pair_dot<6, NX, 6>(d0, d1, B, kM6, mag, x0[o + 4], x1[o + 4]);
+      word_dot<NX>(d0, d1, split6<12, 10>(B, C, kM4, kM6H, mag), x0[o + 5], x1[o + 5]);
+      pair_dot<6, NX, 0>(d0, d1, C, kM6, mag, x0[o + 6], x1[o + 6]);
+      pair_dot<6, NX, 6>(d0, d1, C, kM6, mag, x0[o + 7], x1[o + 7]);
+    }
+  } else if constexpr (BITS == 2) {
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      pair_dot<2, NX, 0>(d0, d1, q[d], kM2, mag, x0[8 * d + 0], x1[8 * d + 0]);
+      pair_dot<2, NX, 2>(d0, d1, q[d], kM2, mag, x0[8 * d + 1], x1[8 * d + 1]);
+      pair_dot<2, NX, 4>(d0, d1, q[d], kM2, mag, x0[8 * d + 2], x1[8 * d + 2]);
+      pair_dot<2, NX, 6>(d0, d1, q[d], kM2, mag, x0[8 * d + 3], x1[8 * d + 3]);
+      pair_dot<2, NX, 8>(d0, d1, q[d], kM2, mag, x0[8 * d + 4], x1[8 * d + 4]);
+      pair_dot<2, NX, 10>(d0, d1, q[d], kM2, mag, x0[8 * d + 5], x1[8 * d + 5]);
+      pair_dot<2, NX, 12>(d0, d1, q[d], kM2, mag, x0[8 * d + 6], x1[8 * d + 6]);
+      pair_dot<2, NX, 14>(d0, d1, q[d], kM2, mag, x0[8 * d + 7], x1[8 * d + 7]);
+    }
+  } else if constexpr (BITS == 3) {
+    // slot s at bit 3s, slot s + 5 at bit 16 + 3s of each word
+#pragma unroll
+    for (int w = 0; w < 5; ++w) {
+      pair_dot<3, NX, 0>(d0, d1, q[w], kM3, mag, x0[5 * w + 0], x1[5 * w + 0]);
+      pair_dot<3, NX, 3>(d0, d1, q[w], kM3, mag, x0[5 * w + 1], x1[5 * w + 1]);
+      pair_dot<3, NX, 6>(d0, d1, q[w], kM3, mag, x0[5 * w + 2], x1[5 * w + 2]);
+      pair_dot<3, NX, 9>(d0, d1, q[w], kM3, mag, x0[5 * w + 3], x1[5 * w + 3]);
+      pair_dot<3, NX, 12>(d0, d1, q[w], kM3, mag, x0[5 * w + 4], x1[5 * w + 4]);
+    }
+  }
+  if constexpr (NX == 2) dot_fence(d0, d1);
+  else dot_fence(d0);
+}
+
+// 8-bit codes as two nibble planes, q = 16 hi + lo: low-plane pairs (128 + lo)
+// into dl, high-plane pairs into dh, for codes (4k+i, 4k+i+2) of dword k.
+template <int NX>
+__device__ __forceinline__ void byte_dots(const uint32_t (&q)[8], const uint32_t (&x0)[16], const uint32_t (&x1)[16],
+                                          float& dl, float& dh) {
+  const uint32_t mag = kMagic;
+  float el = 0.f, eh = 0.f;  // against x1
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    pair_dot<8, NX, 0>(dl, el, q[k], kM4, mag, x0[2 * k], x1[2 * k]);
+    pair_dot<8, NX, 8>(dl, el, q[k], kM4, mag, x0[2 * k + 1], x1[2 * k + 1]);
+    pair_dot<8, NX, 4>(dh, eh, q[k], kM4, mag, x0[2 * k], x1[2 * k]);
+    pair_dot<8, NX, 12>(dh, eh, q[k], kM4, mag, x0[2 * k + 1], x1[2 * k + 1]);
+  }
+  dot_fence(dl, dh);
+  if constexpr (NX == 2) dot_fence(el, eh);
+  if constexpr (NX == 2) {
+    dl += el;
+    dh += eh;
+  }
 }
 
 // Partial sum of one chunk: s*D + b_eff*X, for NX inputs (1 = single, 2 = hi/lo split).
@@ -295,41 +448,16 @@ __device__ __forceinline__ float chunk_partial(const uint32_t (&q)[8], uint32_t 
                                                const uint32_t (&x0)[XWords<BITS>::N], float s0,
                                                const uint32_t (&x1)[XWords<BITS>::N], float s1) {
   const float s = bf16_lo_to_f32(sbw), b = bf16_hi_to_f32(sbw);
+  const float sx = NX == 2 ? s0 + s1 : s0;
   if constexpr (BITS == 8) {
     // sum q x = D_lo + 16 D_hi - (128 + 16*128) X
-    uint32_t pl[16], ph[16];
-    byte_pairs(q, pl, ph);
     float dl = 0.f, dh = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dl = dot2(pl[i], x0[i], dl);
-      dh = dot2(ph[i], x0[i], dh);
-    }
-    float sx = s0;
-    if constexpr (NX == 2) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        dl = dot2(pl[i], x1[i], dl);
-        dh = dot2(ph[i], x1[i], dh);
-      }
-      sx += s1;
-    }
+    byte_dots<NX>(q, x0, x1, dl, dh);
     return fmaf(s, fmaf(16.f, dh, dl), (b - 2176.f * s) * sx);
   } else {
-    constexpr int NW = XWords<BITS>::N;
-    uint32_t p[NW];
-    code_pairs<BITS>(q, p);
     float d0 = 0.f, d1 = 0.f;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      d0 = dot2(p[i], x0[i], d0);
-      if constexpr (NX == 2) d1 = dot2(p[i], x1[i], d1);
-    }
-    float d = d0, sx = s0;
-    if constexpr (NX == 2) {
-      d += d1;
-      sx += s1;
-    }
+    code_dots<BITS, NX>(q, x0, x1, d0, d1);
+    const float d = NX == 2 ? d0 + d1 : d0;
     return fmaf(s, d, (b - 128.f * s) * sx);
   }
 }

@@ -70,23 +70,26 @@ __global__ void gen_codes_kernel(uint8_t* base, int64_t mat_stride, int bits, in
     const int64_t r = w / words_per_row, q = w % words_per_row;
     const uint64_t row0 = (uint64_t)r * cols;
     if (bits == 6) {
-      uint32_t lo0 = 0, lo1 = 0, hi = 0;
+      // dwords A, B, C of the unit; code c = j + 8h goes to half h (bit 16h)
+      uint32_t wa = 0, wb = 0, wc = 0;
       for (int c = 0; c < 16; ++c) {
-        uint32_t v = code_of(sub, tensor, row0 + q * 16 + c, 6);
-        const int d = c >> 3, rr = c & 7, i = rr & 3, s = rr >> 2;
-        if (d == 0) lo0 |= (v & 15u) << (4 * rr);
-        else lo1 |= (v & 15u) << (4 * rr);
-        hi |= (v >> 4) << (2 * (4 * d + i) + 16 * s);
+        const uint32_t v = code_of(sub, tensor, row0 + q * 16 + c, 6);
+        const int h = 16 * (c >> 3), j = c & 7;
+        if (j < 2) wa |= v << (h + 6 * j);
+        else if (j == 2) { wa |= (v & 15u) << (h + 12); wc |= (v >> 4) << (h + 12); }
+        else if (j < 5) wb |= v << (h + 6 * (j - 3));
+        else if (j == 5) { wb |= (v & 15u) << (h + 12); wc |= (v >> 4) << (h + 14); }
+        else wc |= v << (h + 6 * (j - 6));
       }
       uint32_t* o = out + 3 * w;
-      o[0] = lo0;
-      o[1] = lo1;
-      o[2] = hi;
+      o[0] = wa;
+      o[1] = wb;
+      o[2] = wc;
     } else if (bits == 3) {
       uint32_t acc = 0;
       for (int c = 0; c < 10; ++c) {
         const int64_t j = q * 10 + c;
-        if (j < cols) acc |= code_of(sub, tensor, row0 + j, 3) << (3 * c);
+        if (j < cols) acc |= code_of(sub, tensor, row0 + j, 3) << (c < 5 ? 3 * c : 16 + 3 * (c - 5));
       }
       out[w] = acc;
     } else {

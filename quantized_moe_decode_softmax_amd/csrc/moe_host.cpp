@@ -109,14 +109,24 @@ static uint32_t get_bits(const uint8_t* row, int64_t bit, int nbits) {
 // bit position (inside the row) of bit `b` of code j, for each layout
 static int64_t code_bit(int bits, int64_t j, int b) {
   if (bits == 6) {
-    int64_t u = j / 16;
-    int c = (int)(j % 16);
-    int64_t base = u * 96;
-    if (b < 4) return base + 32 * (c / 8) + 4 * (c % 8) + b;
-    int d = c / 8, r = c % 8, i = r % 4, sgn = r / 4;
-    return base + 64 + 2 * (4 * d + i) + 16 * sgn + (b - 4);
+    // unit of 16 codes in dwords A, B, C; code c = jj + 8h sits in half h
+    const int64_t u = j / 16;
+    const int c = (int)(j % 16), h = c / 8, jj = c % 8;
+    const int64_t base = u * 96 + 16 * h;
+    int word, rel;
+    switch (jj) {
+      case 0: case 1: word = 0; rel = 6 * jj + b; break;
+      case 3: case 4: word = 1; rel = 6 * (jj - 3) + b; break;
+      case 6: case 7: word = 2; rel = 6 * (jj - 6) + b; break;
+      case 2: word = b < 4 ? 0 : 2; rel = b < 4 ? 12 + b : 12 + (b - 4); break;
+      default: word = b < 4 ? 1 : 2; rel = b < 4 ? 12 + b : 14 + (b - 4); break;  // jj == 5
+    }
+    return base + 32 * word + rel;
   }
-  if (bits == 3) return 32 * (j / 10) + 3 * (j % 10) + b;
+  if (bits == 3) {  // slot l < 5 at bit 3l, slot l >= 5 at bit 16 + 3(l - 5)
+    const int l = (int)(j % 10);
+    return 32 * (j / 10) + (l < 5 ? 3 * l : 16 + 3 * (l - 5)) + b;
+  }
   return (int64_t)bits * j + b;
 }
 

@@ -131,7 +131,7 @@ __device__ __forceinline__ void h_lane(const PArgs& a, bool first, uint32_t ep, 
     uint32_t n[16];
     h_chunk(a, first, ep, t, c, n);
     arrange_chunk<BITS>(n, c, x.w[m]);
-    x.s[m] = sum16(n);
+    x.s[m] = sum_words<XWords<BITS>::N>(x.w[m]);
   }
 }
 
@@ -146,103 +146,79 @@ struct PTaskRows {
 };
 
 // ------------------------------------------------------------- phase A
+// One router row per lane group (rows task * rpw + sr): the router is short
+// (E rows), so one row per wave keeps the per-wave instruction chain short.
 template <int BITS, int CPL>
 __device__ __forceinline__ void router_rows(const PArgs& a, const uint8_t* layer, bool first, uint32_t ep, int task,
                                             int li, int lpr, int sr, int rpw) {
-  constexpr int R = PTaskRows<CPL>::R;
   constexpr int AB = BITS == kDense ? kDense : BITS;
   opaque_lane(li, sr);
-  int rows[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int e = task * R * rpw + sr + rpw * r;
-    rows[r] = e < a.E ? e : -1;
-  }
-  float out[R];
+  const int e = task * rpw + sr;
+  const int row = e < a.E ? e : -1;
+  float out[1];
   XLane<AB, CPL> x;
-  // the shared-expert gate vector, in x's arrangement (task 0 only)
-  XLane<AB, CPL> g;
-  const bool stats = task == 0;
-  if (stats) {
-    const uint16_t* gv = (const uint16_t*)(layer + a.off_gatevec);
-#pragma unroll
-    for (int m = 0; m < CPL; ++m) {
-      const int c = li + lpr * m;
-      uint32_t n[16];
-      if (c < (a.H >> 5)) {
-        load64B(gv + 32 * c, n);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) n[i] = 0u;
-      }
-      arrange_chunk<AB>(n, c, g.w[m]);
-    }
-  }
   if constexpr (BITS == kDense) {
     const uint16_t* w = (const uint16_t*)(layer + a.off_router);
-    const uint16_t* rp[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) rp[r] = rows[r] >= 0 ? w + (int64_t)rows[r] * a.H : nullptr;
-    RowsD<CPL, R> Q;
-    load_dense_rows<CPL, R>(Q, rp, a.H, li, lpr);
+    const uint16_t* rp[1] = {row >= 0 ? w + (int64_t)row * a.H : nullptr};
+    RowsD<CPL, 1> Q;
+    load_dense_rows<CPL, 1>(Q, rp, a.H, li, lpr);
     for (int t = 0; t < a.T; ++t) {
       h_lane<AB, CPL>(a, first, ep - 1, t, li, lpr, x);
-      dot_dense_rows<CPL, R>(Q, x, out);
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float v = reduce_row(out[r], lpr);
-        if (rows[r] >= 0 && li == lpr - 1) st_tag(a.tg_logit + (int64_t)t * a.E + rows[r], __float_as_uint(v), ep);
-      }
-      if (stats) {
-        float gd = 0.f;
-#pragma unroll
-        for (int m = 0; m < CPL; ++m)
-#pragma unroll
-          for (int i = 0; i < XWords<AB>::N; ++i) gd = dot2(x.w[m][i], g.w[m][i], gd);
-        const float ss = reduce_row(sumsq(x), lpr);
-        gd = reduce_row(gd, lpr);
-        if (sr == 0 && li == lpr - 1) {
-          const float rr = rms_factor(ss, a.H, a.eps);
-          st_tag(a.tg_rs + 2 * t, __float_as_uint(rr), ep);
-          st_tag(a.tg_rs + 2 * t + 1, __float_as_uint(1.0f / (1.0f + expf(-(rr * gd)))), ep);
-        }
-      }
+      dot_dense_rows<CPL, 1>(Q, x, out);
+      const float v = reduce_row(out[0], lpr);
+      if (row >= 0 && li == lpr - 1) st_tag(a.tg_logit + (int64_t)t * a.E + row, __float_as_uint(v), ep);
     }
   } else {
     const uint8_t* base = layer + a.off_router;
     const int64_t rb = row_bytes(BITS, a.H);
     const uint32_t* sb = (const uint32_t*)(base + matrix_codes_bytes(BITS, a.E, a.H));
-    const uint8_t* rc[R];
-    const uint32_t* rs[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      rc[r] = rows[r] >= 0 ? base + (int64_t)rows[r] * rb : nullptr;
-      rs[r] = rows[r] >= 0 ? sb + (int64_t)rows[r] * (a.H >> 6) : nullptr;
-    }
-    RowsQ<BITS, CPL, R> Q;
-    load_rows<BITS, CPL, R>(Q, rc, rs, a.H, (int)(rb >> 2), li, lpr);
+    const uint8_t* rc[1] = {row >= 0 ? base + (int64_t)row * rb : nullptr};
+    const uint32_t* rs[1] = {row >= 0 ? sb + (int64_t)row * (a.H >> 6) : nullptr};
+    RowsQ<BITS, CPL, 1> Q;
+    load_rows<BITS, CPL, 1>(Q, rc, rs, a.H, (int)(rb >> 2), li, lpr);
     for (int t = 0; t < a.T; ++t) {
       h_lane<BITS, CPL>(a, first, ep - 1, t, li, lpr, x);
-      dot_rows<BITS, CPL, R, 1>(Q, x, x, out);
+      dot_rows<BITS, CPL, 1, 1>(Q, x, x, out);
+      const float v = reduce_row(out[0], lpr);
+      if (row >= 0 && li == lpr - 1) st_tag(a.tg_logit + (int64_t)t * a.E + row, __float_as_uint(v), ep);
+    }
+  }
+}
+
+// RMS factor and shared-expert gate of every token row (one task), from h in
+// the router's arrangement AB (the per-layer kernels use the same order):
+// ss = sum of squares, gate = sigmoid(r * gvec . h).
+template <int AB, int CPL>
+__device__ __forceinline__ void stats_rows(const PArgs& a, const uint8_t* layer, bool first, uint32_t ep, int li,
+                                           int lpr, int sr) {
+  opaque_lane(li, sr);
+  XLane<AB, CPL> x, g;
+  const uint16_t* gv = (const uint16_t*)(layer + a.off_gatevec);
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float v = reduce_row(out[r], lpr);
-        if (rows[r] >= 0 && li == lpr - 1) st_tag(a.tg_logit + (int64_t)t * a.E + rows[r], __float_as_uint(v), ep);
-      }
-      if (stats) {
-        float gd = 0.f;
+  for (int m = 0; m < CPL; ++m) {
+    const int c = li + lpr * m;
+    uint32_t n[16];
+    if (c < (a.H >> 5)) {
+      load64B(gv + 32 * c, n);
+    } else {
 #pragma unroll
-        for (int m = 0; m < CPL; ++m)
+      for (int i = 0; i < 16; ++i) n[i] = 0u;
+    }
+    arrange_chunk<AB>(n, c, g.w[m]);
+  }
+  for (int t = 0; t < a.T; ++t) {
+    h_lane<AB, CPL>(a, first, ep - 1, t, li, lpr, x);
+    float gd = 0.f;
 #pragma unroll
-          for (int i = 0; i < XWords<BITS>::N; ++i) gd = dot2(x.w[m][i], g.w[m][i], gd);
-        const float ss = reduce_row(sumsq(x), lpr);
-        gd = reduce_row(gd, lpr);
-        if (sr == 0 && li == lpr - 1) {
-          const float rr = rms_factor(ss, a.H, a.eps);
-          st_tag(a.tg_rs + 2 * t, __float_as_uint(rr), ep);
-          st_tag(a.tg_rs + 2 * t + 1, __float_as_uint(1.0f / (1.0f + expf(-(rr * gd)))), ep);
-        }
-      }
+    for (int m = 0; m < CPL; ++m)
+#pragma unroll
+      for (int i = 0; i < XWords<AB>::N; ++i) gd = dot2(x.w[m][i], g.w[m][i], gd);
+    const float ss = reduce_row(sumsq(x), lpr);
+    gd = reduce_row(gd, lpr);
+    if (sr == 0 && li == lpr - 1) {
+      const float rr = rms_factor(ss, a.H, a.eps);
+      st_tag(a.tg_rs + 2 * t, __float_as_uint(rr), ep);
+      st_tag(a.tg_rs + 2 * t + 1, __float_as_uint(1.0f / (1.0f + expf(-(rr * gd)))), ep);
     }
   }
 }
@@ -340,23 +316,16 @@ __device__ __forceinline__ void down_rows(const PArgs& a, uint32_t ep, const uin
 #pragma unroll
     for (int m = 0; m < CPL; ++m) {
       const int c = li + lpr * m;
-      uint32_t hn[16], ln[16];
+      uint32_t w[32];
       if (c < nch) {
-        uint32_t w[32];
         poll_words<32>(src + c, a.imax >> 5, ep, w, a.status);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          hn[i] = (w[2 * i] & 0xFFFFu) | (w[2 * i + 1] << 16);
-          ln[i] = (w[2 * i] >> 16) | (w[2 * i + 1] & 0xFFFF0000u);
-        }
       } else {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) hn[i] = ln[i] = 0u;
+        for (int i = 0; i < 32; ++i) w[i] = 0u;
       }
-      arrange_chunk<BITS>(hn, c, xh.w[m]);
-      arrange_chunk<BITS>(ln, c, xl.w[m]);
-      xh.s[m] = sum16(hn);
-      xl.s[m] = sum16(ln);
+      split_arrange<BITS>(w, c, xh.w[m], xl.w[m]);
+      xh.s[m] = sum_words<XWords<BITS>::N>(xh.w[m]);
+      xl.s[m] = sum_words<XWords<BITS>::N>(xl.w[m]);
     }
     dot_rows<BITS, CPL, RD, 2>(Q, xh, xl, out);
 #pragma unroll
@@ -373,10 +342,11 @@ __device__ __forceinline__ void down_rows(const PArgs& a, uint32_t ep, const uin
 // experts' row masks in LDS.
 template <int M>
 __device__ __forceinline__ void route_row(const PArgs& a, int t, uint32_t ep, int* s_ids, float* s_w,
-                                          uint32_t* s_emask, float* s_r) {
+                                          uint32_t* s_emask, float* s_r, float* s_sg, int* s_units,
+                                          uint32_t* s_masks) {
   const int lane = threadIdx.x & 63;
   uint32_t rv[M];
-  uint32_t rr = 0u;
+  uint32_t rr = 0u, rg = 0u;
   uint32_t spins = 0;
   while (true) {  // all logits of the row and its RMS factor, polled together
     bool ok = true;
@@ -393,6 +363,9 @@ __device__ __forceinline__ void route_row(const PArgs& a, int t, uint32_t ep, in
     const uint64_t v = ld_tag(a.tg_rs + 2 * t);
     rr = (uint32_t)v;
     ok &= (uint32_t)(v >> 32) == ep;
+    const uint64_t vg = ld_tag(a.tg_rs + 2 * t + 1);
+    rg = (uint32_t)vg;
+    ok &= (uint32_t)(vg >> 32) == ep;
     if (__all(ok)) break;
     ++spins;
     if ((spins & 63) == 0) {
@@ -414,9 +387,17 @@ __device__ __forceinline__ void route_row(const PArgs& a, int t, uint32_t ep, in
   if (lane < a.k) {
     s_ids[t * kMaxTopK + lane] = my_id;
     s_w[t * kMaxTopK + lane] = my_w;
-    atomicOr(&s_emask[my_id], 1u << t);
+    if (a.T == 1) {  // one row: its k experts are the units, in rank order
+      s_units[lane] = my_id;
+      s_masks[lane] = 1u;
+    } else {
+      atomicOr(&s_emask[my_id], 1u << t);
+    }
   }
-  if (lane == 0) s_r[t] = r;
+  if (lane == 0) {
+    s_r[t] = r;
+    s_sg[t] = __uint_as_float(rg);
+  }
 }
 
 #define MOE_PBITS(bits, B, ...)                        \
@@ -433,6 +414,7 @@ __global__ void __launch_bounds__(kPThreads) stack_kernel(PArgs a) {
   __shared__ int s_ids[kMaxT * kMaxTopK];
   __shared__ float s_w[kMaxT * kMaxTopK];
   __shared__ float s_r[kMaxT];
+  __shared__ float s_sg[kMaxT];
   __shared__ uint32_t s_emask[kMaxExperts];
   __shared__ int s_units[kMaxT * kMaxTopK];
   __shared__ uint32_t s_masks[kMaxT * kMaxTopK];
@@ -461,23 +443,31 @@ __global__ void __launch_bounds__(kPThreads) stack_kernel(PArgs a) {
     const uint32_t ep = (uint32_t)l + 1;
     const bool first = l == 0;
     // ---------------- phase A: router rows, shared-expert SwiGLU, row stats
-    for (int task = gw; task < a.n_rt + a.n_st; task += n_gw) {
+    for (int task = gw; task < a.n_rt + 1 + a.n_st; task += n_gw) {
       if (task < a.n_rt) {
         if (a.rbits == kDense) {
           router_rows<kDense, CPL_H>(a, layer, first, ep, task, li_h, lpr_h, sr_h, rpw_h);
         } else {
           MOE_PBITS(a.rbits, B, router_rows<B, CPL_H>(a, layer, first, ep, task, li_h, lpr_h, sr_h, rpw_h));
         }
+      } else if (task == a.n_rt) {
+        if (a.rbits == kDense) {
+          stats_rows<kDense, CPL_H>(a, layer, first, ep, li_h, lpr_h, sr_h);
+        } else {
+          MOE_PBITS(a.rbits, B, stats_rows<B, CPL_H>(a, layer, first, ep, li_h, lpr_h, sr_h));
+        }
       } else {
-        const int i0 = (task - a.n_rt) * RP * rpw_h;
+        const int i0 = (task - a.n_rt - 1) * RP * rpw_h;
         MOE_PBITS(a.sbits, B,
                   swiglu_rows<B, CPL_H>(a, first, ep, layer + a.off_shared, a.off_shared_up, a.Is, i0, all_rows, a.k,
                                         -1, nullptr, nullptr, li_h, lpr_h, sr_h, rpw_h));
       }
     }
     // ---------------- phase B: routing (every workgroup), routed SwiGLU rows
-    for (int e = tid; e < a.E; e += kPThreads) s_emask[e] = 0u;
-    __syncthreads();
+    if (a.T > 1) {
+      for (int e = tid; e < a.E; e += kPThreads) s_emask[e] = 0u;
+      __syncthreads();
+    }
     if (sh_in_b && wave == kPWaves - 1 && j0 < a.H) {
       // shared-expert down rows on a wave that has no routing row
       const uint8_t* mat = layer + a.off_shared + a.off_shared_down;
@@ -485,15 +475,15 @@ __global__ void __launch_bounds__(kPThreads) stack_kernel(PArgs a) {
     }
     for (int t = wave; t < a.T; t += kPWaves) {
       switch (a.mE) {
-        case 1: route_row<1>(a, t, ep, s_ids, s_w, s_emask, s_r); break;
-        case 2: route_row<2>(a, t, ep, s_ids, s_w, s_emask, s_r); break;
-        case 4: route_row<4>(a, t, ep, s_ids, s_w, s_emask, s_r); break;
-        default: route_row<8>(a, t, ep, s_ids, s_w, s_emask, s_r); break;
+        case 1: route_row<1>(a, t, ep, s_ids, s_w, s_emask, s_r, s_sg, s_units, s_masks); break;
+        case 2: route_row<2>(a, t, ep, s_ids, s_w, s_emask, s_r, s_sg, s_units, s_masks); break;
+        case 4: route_row<4>(a, t, ep, s_ids, s_w, s_emask, s_r, s_sg, s_units, s_masks); break;
+        default: route_row<8>(a, t, ep, s_ids, s_w, s_emask, s_r, s_sg, s_units, s_masks); break;
       }
     }
     __syncthreads();
-    int base = 0;
-    for (int e0 = 0; e0 < a.E; e0 += kPThreads) {
+    int base = a.T == 1 ? a.k : 0;
+    for (int e0 = 0; a.T > 1 && e0 < a.E; e0 += kPThreads) {
       const int e = e0 + tid;
       const bool used = e < a.E && s_emask[e] != 0u;
       const unsigned long long bal = __ballot(used);
@@ -544,9 +534,7 @@ __global__ void __launch_bounds__(kPThreads) stack_kernel(PArgs a) {
       const int npair = J >> 1;
       for (int i = tid; i < a.T * npair; i += kPThreads) {
         const int t = i / npair, q = 2 * (i % npair);
-        uint32_t sgv[1];
-        poll_words<1>(a.tg_rs + 2 * t + 1, 0, ep, sgv, a.status);
-        const float sg = __uint_as_float(sgv[0]);
+        const float sg = s_sg[t];
         uint32_t o[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {

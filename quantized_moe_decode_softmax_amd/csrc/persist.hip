@@ -70,7 +70,7 @@ int32_t launch_stack_persistent(const moe_shape_t& s, const moe_layer_layout_t& 
   if (RD > (cpl_i == 2 ? 2 : 8)) return MOE_ERR_UNSUPPORTED;
   const int rpw_h = 64 / lanes_per_row(s.hidden);
   const int R = cpl_h >= 2 ? 2 : 4;
-  a.n_rt = (a.E + R * rpw_h - 1) / (R * rpw_h);
+  a.n_rt = (a.E + rpw_h - 1) / rpw_h;  // one router row per lane group
   a.n_st = (a.Is + (R / 2) * rpw_h - 1) / ((R / 2) * rpw_h);
   a.tpu = (a.I + (R / 2) * rpw_h - 1) / ((R / 2) * rpw_h);
   a.mE = pow2ceil((a.E + 63) / 64);

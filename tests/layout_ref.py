@@ -39,21 +39,32 @@ def unpack(bits: int, rows: int, cols: int, buf: np.ndarray):
     elif bits == 2:
         codes = np.stack([(raw >> s) & 3 for s in (0, 2, 4, 6)], axis=-1).reshape(rows, cols)
     elif bits == 6:
+        # unit of 16 codes in dwords A, B, C; code c = j + 8h in half h:
+        # j 0,1 / 3,4 / 6,7: 6 bits at A / B / C bit 6*(j mod 3); j 2 / 5: low
+        # nibble at A / B bit 12, high 2 bits at C bit 12 / 14
         w = raw.view(np.uint32).reshape(rows, cols // 16, 3).astype(np.uint64)
         codes = np.zeros((rows, cols // 16, 16), dtype=np.uint8)
+
+        def field(word, bit, n):
+            return (w[..., word] >> np.uint64(bit)) & np.uint64((1 << n) - 1)
+
         for c in range(16):
-            d, r = divmod(c, 8)
-            i, s = r % 4, r // 4
-            lo = (w[..., d] >> np.uint64(4 * r)) & np.uint64(15)
-            hi = (w[..., 2] >> np.uint64(2 * (4 * d + i) + 16 * s)) & np.uint64(3)
-            codes[..., c] = (lo | (hi << np.uint64(4))).astype(np.uint8)
+            h, j = 16 * (c // 8), c % 8
+            if j in (2, 5):
+                v = field(j // 3, h + 12, 4) | (field(2, h + 12 + 2 * (j // 5), 2) << np.uint64(4))
+            else:
+                v = field(j // 3, h + 6 * (j % 3), 6)
+            codes[..., c] = v.astype(np.uint8)
         codes = codes.reshape(rows, cols)
     elif bits == 3:
+        # 10 codes per dword: slot l < 5 at bit 3l, slot l >= 5 at bit 16 + 3(l - 5)
         w = raw.view(np.uint32).astype(np.uint64)
         j = np.arange(cols)
-        codes = ((w[:, j // 10] >> np.uint64(3) * (j % 10).astype(np.uint64)) & np.uint64(7)).astype(np.uint8)
-        # spare bits and unused slots must be zero
-        assert np.all(w >> np.uint64(30) == 0)
+        l = j % 10
+        pos = np.where(l < 5, 3 * l, 16 + 3 * (l - 5)).astype(np.uint64)
+        codes = ((w[:, j // 10] >> pos) & np.uint64(7)).astype(np.uint8)
+        # spare bits (15 and 31) must be zero
+        assert np.all(w & np.uint64(0x80008000) == 0)
     else:
         raise ValueError(bits)
     sb = buf[codes_bytes(bits, rows, cols): codes_bytes(bits, rows, cols) + rows * (cols // GROUP) * 4]

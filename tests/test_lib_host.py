@@ -175,16 +175,20 @@ def test_pack_known_words():
     codes[0, :8] = np.arange(1, 9)
     p = moe.moe_pack_matrix(4, codes, np.zeros((1, 1), np.uint16), np.zeros((1, 1), np.uint16))
     assert p[:4].view(np.uint32)[0] == 0x87654321
-    # 3 bits: 10 codes of 7 fill bits 0..29 of the first dword
+    # 3 bits: 10 codes of 7 fill bits 0..14 and 16..30 of the first dword; code 12 (slot 2) -> bit 6 of dword 1
     codes = np.zeros((1, 64), dtype=np.uint8)
     codes[0, :10] = 7
+    codes[0, 12] = 5
     p = moe.moe_pack_matrix(3, codes, np.zeros((1, 1), np.uint16), np.zeros((1, 1), np.uint16))
-    assert p[:8].view(np.uint32).tolist() == [0x3FFFFFFF, 0]
-    # 6 bits: code 63 at local index 5 -> low nibble at bits 20..23 of dword 0, high bits at 2*(0*4+1)+16 = 18
+    assert p[:8].view(np.uint32).tolist() == [0x7FFF7FFF, 5 << 6]
+    # 6 bits: code 63 at local index 5 -> low nibble at bits 12..15 of dword B, high bits at 14..15 of dword C;
+    # at local index 9 (j = 1, upper half) -> bits 16 + 6 .. 16 + 11 of dword A; index 14 (j = 6) -> C bits 16..21
     codes = np.zeros((1, 64), dtype=np.uint8)
     codes[0, 5] = 63
+    codes[0, 9] = 0x2A
+    codes[0, 14] = 0x15
     p = moe.moe_pack_matrix(6, codes, np.zeros((1, 1), np.uint16), np.zeros((1, 1), np.uint16))
-    assert p[:12].view(np.uint32).tolist() == [0xF << 20, 0, 3 << 18]
+    assert p[:12].view(np.uint32).tolist() == [0x2A << 22, 0xF << 12, (3 << 14) | (0x15 << 16)]
     # scale/bias dword: scale in the low half
     p = moe.moe_pack_matrix(8, np.zeros((1, 64), np.uint8), np.array([[0x3F80]], np.uint16),
                             np.array([[0xBF00]], np.uint16))
