@@ -628,13 +628,21 @@ extern "C" int32_t moe_decode_stack(const moe_shape_t* shape, const void* const*
     hipError_t e = hipMemcpyAsync(h_trace_dev, h_in_dev, th * 2, hipMemcpyDeviceToDevice, st);
     if (e != hipSuccess) return set_error(MOE_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
   }
-  // one persistent kernel per up to 64 layers when the shape allows it
-  // (MOE_STACK_KERNEL=0 selects the per-layer kernels, for comparison)
-  static const bool use_stack_kernel = [] {
+  // One persistent kernel per up to 64 layers when the shape allows it: the
+  // one-row streaming kernel, else the general one. MOE_STACK_KERNEL selects
+  // a path for comparison: 0 = per-layer kernels only, 1 = never the
+  // streaming kernel. All paths give the same results bit for bit.
+  static const int stack_kernel_mode = [] {
     const char* v = getenv("MOE_STACK_KERNEL");
-    return !(v && v[0] == '0');
+    return v && (v[0] == '0' || v[0] == '1') ? v[0] - '0' : 2;
   }();
-  if (use_stack_kernel) {
+  if (stack_kernel_mode == 2) {
+    rc = launch_stack_t1(*shape, L, m, (uint8_t*)ws_dev, layers_host, n_layers, T, h_in_dev, h_out_dev, ids_dev,
+                         w_dev, h_trace_dev, st);
+    if (rc != MOE_ERR_UNSUPPORTED) return rc;
+    clear_error();
+  }
+  if (stack_kernel_mode >= 1) {
     rc = launch_stack_persistent(*shape, L, m, (uint8_t*)ws_dev, layers_host, n_layers, T, h_in_dev, h_out_dev,
                                  ids_dev, w_dev, h_trace_dev, st);
     if (rc != MOE_ERR_UNSUPPORTED) return rc;

@@ -649,8 +649,10 @@ __device__ __forceinline__ int wave_min_i(int v) {
 // Each lane first sorts its M values (key descending, index ascending); each
 // round takes the wave maximum of the lanes' list heads; if several lanes hold
 // that key, the lowest index among them wins; the winner pops its head.
-template <int M>
+// KF: k when known at compile time (0: k <= kMaxTopK at run time).
+template <int M, int KF = 0>
 __device__ __forceinline__ void topk_select(int (&key)[M], int k, int& lane_id, float& lane_w) {
+  constexpr int KMAX = KF ? KF : kMaxTopK;
   const int lane = threadIdx.x & 63;
   int idx[M];
 #pragma unroll
@@ -669,11 +671,11 @@ __device__ __forceinline__ void topk_select(int (&key)[M], int k, int& lane_id, 
     }
   // k rounds of wave max; the selected logits are wave-uniform, lane i keeps
   // round i's (id, logit) so no per-lane array is ever indexed by the lane
-  float sel[kMaxTopK];
+  float sel[KMAX];
   float my_sel = -INFINITY;
   lane_id = 0;
 #pragma unroll
-  for (int i = 0; i < kMaxTopK; ++i) {
+  for (int i = 0; i < KMAX; ++i) {
     sel[i] = -INFINITY;
     if (i < k) {
       const int mx = wave_max_i(key[0]);
@@ -704,7 +706,7 @@ __device__ __forceinline__ void topk_select(int (&key)[M], int k, int& lane_id, 
   const float mx = sel[0];
   float sum = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxTopK; ++i)
+  for (int i = 0; i < KMAX; ++i)
     if (i < k) sum += expf(sel[i] - mx);  // uniform branch
   lane_w = lane < k ? expf(my_sel - mx) / sum : 0.f;
 }

@@ -23,20 +23,22 @@ constexpr int kMaxExperts = 512;
 constexpr int kMaxDim = 8192;
 constexpr int kMaxLayersPerLaunch = 64;
 constexpr int64_t kAlign = 256;
+// copies of each exchange buffer of the streaming stack kernel (one per XCD)
+constexpr int kExchangeCopies = 8;
 
-MOE_HD inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+MOE_HD constexpr inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 // bytes of one row of codes
-MOE_HD inline int64_t row_bytes(int bits, int cols) {
+MOE_HD constexpr inline int64_t row_bytes(int bits, int cols) {
   if (bits == 3) return 4 * (((int64_t)cols + 9) / 10);
   return (int64_t)cols * bits / 8;
 }
-MOE_HD inline bool bits_ok(int bits) { return bits == 2 || bits == 3 || bits == 4 || bits == 6 || bits == 8; }
+MOE_HD constexpr inline bool bits_ok(int bits) { return bits == 2 || bits == 3 || bits == 4 || bits == 6 || bits == 8; }
 
 // offsets inside one packed matrix block
-MOE_HD inline int64_t matrix_codes_bytes(int bits, int rows, int cols) { return align_up(row_bytes(bits, cols) * rows, kAlign); }
-MOE_HD inline int64_t matrix_sb_bytes(int rows, int cols) { return align_up((int64_t)rows * (cols / kGroup) * 4, kAlign); }
-MOE_HD inline int64_t matrix_bytes(int bits, int rows, int cols) {
+MOE_HD constexpr inline int64_t matrix_codes_bytes(int bits, int rows, int cols) { return align_up(row_bytes(bits, cols) * rows, kAlign); }
+MOE_HD constexpr inline int64_t matrix_sb_bytes(int rows, int cols) { return align_up((int64_t)rows * (cols / kGroup) * 4, kAlign); }
+MOE_HD constexpr inline int64_t matrix_bytes(int bits, int rows, int cols) {
   return matrix_codes_bytes(bits, rows, cols) + matrix_sb_bytes(rows, cols);
 }
 
@@ -58,6 +60,15 @@ struct WsMap {
   int64_t tg_logit;     // u64 [T][E]         raw router dot products
   int64_t tg_rs;        // u64 [T][2]         RMS factor, shared-expert gate
   int64_t tg_a;         // u64 [T][k+1][Imax] activations, bf16 hi | bf16 lo << 16
+  // one-row streaming stack kernel (stack1.hip): the same word format, each
+  // buffer in n_copy copies (stride *_cs words) that writers all store and
+  // workgroup w reads copy w % n_copy; sized for one token row
+  int n_copy;
+  int64_t x_h;          // u64 [2][n_copy][H/2]      hidden state by layer parity
+  int64_t x_logit;      // u64 [n_copy][E]           raw router dot products
+  int64_t x_a;          // u64 [n_copy][k+1][Imax]   activations, bf16 hi | bf16 lo << 16
+  int64_t x_flag;       // u64 [n_copy][512]         per workgroup: its activations are stored
+  int64_t xh_cs, xl_cs, xa_cs;
   int64_t status;       // u32 [64]           word 0: nonzero after a timed-out wait
   int64_t tg_end;       // end of the region the stack kernel clears per call
   int64_t total;
@@ -78,5 +89,11 @@ int32_t launch_stack_persistent(const moe_shape_t& s, const moe_layer_layout_t& 
                                 const void* const* layers, int n_layers, int T, const uint16_t* h_in, uint16_t* h_out,
                                 int32_t* ids_out, float* w_out, uint16_t* h_trace_out, moe_stream_t st);
 void layout_of(const moe_shape_t& s, moe_layer_layout_t* out);
+
+// One-row stack decode with the streaming kernel (stack1.hip).
+// MOE_ERR_UNSUPPORTED, with nothing launched, for calls it does not handle.
+int32_t launch_stack_t1(const moe_shape_t& s, const moe_layer_layout_t& L, const WsMap& m, uint8_t* ws,
+                        const void* const* layers, int n_layers, int T, const uint16_t* h_in, uint16_t* h_out,
+                        int32_t* ids_out, float* w_out, uint16_t* h_trace_out, moe_stream_t st);
 
 }  // namespace moe

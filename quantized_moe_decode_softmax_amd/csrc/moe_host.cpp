@@ -89,6 +89,14 @@ WsMap ws_map(const moe_shape_t& s, int T) {
   m.tg_logit = take((int64_t)T * s.n_experts * 8);
   m.tg_rs = take((int64_t)T * 2 * 8);
   m.tg_a = take((int64_t)T * (k + 1) * imax * 8);
+  m.n_copy = kExchangeCopies;
+  m.xh_cs = align_up(s.hidden / 2, 512);
+  m.xl_cs = align_up(s.n_experts, 512);
+  m.xa_cs = align_up((int64_t)(k + 1) * imax, 512);
+  m.x_h = take(2 * m.n_copy * m.xh_cs * 8);
+  m.x_logit = take(m.n_copy * m.xl_cs * 8);
+  m.x_a = take(m.n_copy * m.xa_cs * 8);
+  m.x_flag = take(m.n_copy * 512 * 8);
   m.status = take(64 * 4);
   m.tg_end = off;
   m.total = off;
