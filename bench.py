@@ -12,14 +12,19 @@ row per step (seed 1000 + step). Prints one JSON line:
   the routing the GPU returned; duplicates across rows counted once), the
   shared expert, the router and the gate vector, at their packed size
   (codes + one bf16 scale and bias per 64 weights);
-* roofline: the dominant kernel, the persistent stack kernel (one launch per
-  step runs all layers, preceded by a small clear kernel), against the 8 TB/s
-  HBM peak: touched bytes per launch / mean launch duration, the duration
-  taken with HIP events recorded around every step on the stream the library
-  launches on;
+* roofline: the dominant kernel, the streaming stack kernel (one launch per
+  step runs all layers, preceded by a clear kernel of about 2 us), against the
+  8 TB/s HBM peak: touched bytes per launch / mean launch duration, the
+  duration taken with HIP events recorded around every step on the stream the
+  library launches on; traffic: the HBM bytes one launch fetched and wrote,
+  from rocprofv3 FETCH_SIZE and WRITE_SIZE passes scaled by what the same
+  counters read for a plain device copy of known size (--copy-probe), stored
+  below with a hash of the kernel sources and reported only while the sources
+  still hash the same;
 * cpu_baseline: the fp64 oracle timed on this host on a bounded sample.
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload a3b] [--no-cpu]
+       python bench.py --copy-probe MIB   (PMC calibration: 5 device copies)
 """
 
 from __future__ import annotations
@@ -33,6 +38,41 @@ import time
 import numpy as np
 
 HBM_PEAK_GBPS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ["stack1.hip", "gemv.h", "internal.h", "decode.hip"]
+
+# HBM traffic of one stack-kernel launch, from two rocprofv3 --pmc passes
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) over
+# `bench.py --steps 5 --warmup 2 --no-cpu`, each scaled by bytes/counter of a
+# 256 MiB device copy measured the same way. Keyed by workload; valid only
+# for the kernel sources whose hash is stored with it.
+TRAFFIC = {
+    "a3b": {"src_hash": "c9c10d40818c7c64", "fetch_bytes": 997_120_343, "write_bytes": 55_063_859},
+}
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "quantized_moe_decode_softmax_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def copy_probe(mib: int) -> int:
+    """Five copies of a MIB-MiB device buffer: the known-size kernel the PMC byte counters are scaled by."""
+    import torch
+
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "copies": 5}), flush=True)
+    return 0
 
 
 def _matrix_alg_bytes(bits: int, rows: int, cols: int) -> int:
@@ -58,7 +98,7 @@ def touched_bytes(w, ids: np.ndarray) -> int:
 
 
 def cpu_baseline(w, budget_s: float = 15.0):
-    """The oracle as it stands, one token through as many layers as fit the budget."""
+    """The oracle as it stands: token rows through the layer stack, in order, until the budget is spent."""
     import oracle
     from oracle.gen import GeneratedLayer, MoEShape, gen_x
 
@@ -73,15 +113,18 @@ def cpu_baseline(w, budget_s: float = 15.0):
     if ctx:
         ctx.__enter__()
     try:
-        h = gen_x(1000, 1, w.hidden)
         t0 = time.perf_counter()
-        n = 0
-        while n < w.n_layers:
-            r = oracle.layer_forward(GeneratedLayer(sh, 0, n), h)
-            h = oracle.bf16_round(r["y"])
-            n += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
+        n = 0  # layer passes done
+        tokens = 0
+        while time.perf_counter() - t0 < budget_s:
+            h = gen_x(1000 + tokens, 1, w.hidden)
+            for layer in range(w.n_layers):
+                r = oracle.layer_forward(GeneratedLayer(sh, 0, layer), h)
+                h = oracle.bf16_round(r["y"])
+                n += 1
+                if time.perf_counter() - t0 > budget_s:
+                    break
+            tokens += 1
         dt = time.perf_counter() - t0
     finally:
         if ctx:
@@ -92,9 +135,9 @@ def cpu_baseline(w, budget_s: float = 15.0):
         "unit": "tok/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"1 token (x seed 1000) through the first {n} of {w.n_layers} layers in {dt:.1f} s, "
-                   f"fp64 numpy incl. regenerating the selected experts, BLAS limited to 1 thread; "
-                   f"scaled to {w.n_layers} layers"),
+        "sample": (f"{n} layer passes ({tokens} token(s), x seeds from 1000, through the {w.n_layers}-layer "
+                   f"stack in order) in {dt:.1f} s, fp64 numpy incl. regenerating the selected experts, BLAS "
+                   f"limited to 1 thread; scaled to {w.n_layers} layers per token"),
         "host_cpus": os.cpu_count(),
     }
 
@@ -107,11 +150,14 @@ def main() -> int:
     ap.add_argument("--workload", default="a3b")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding of this "
               "path is a design note, not a measured configuration", file=sys.stderr)
         return 2
+    if args.copy_probe:
+        return copy_probe(args.copy_probe)
 
     import torch
 
@@ -155,6 +201,12 @@ def main() -> int:
     tok_s = T * K / wall
     gbps = tb / (wall * 1e9)
     kernel_gbps = tb / K / launch_s / 1e9
+    tr = TRAFFIC.get(args.workload)
+    traffic = traffic_detail = None
+    if tr is not None and tr["src_hash"] == kernel_source_hash():
+        traffic = tr["fetch_bytes"] + tr["write_bytes"]
+        traffic_detail = {"fetch_bytes": tr["fetch_bytes"], "write_bytes": tr["write_bytes"],
+                          "vs_touched_bytes": round(traffic / (tb / K), 3)}
     res = {
         "metric": "MoE-stack decode tokens/s + achieved HBM GB/s on touched expert bytes vs 8 TB/s",
         "value": round(tok_s, 2),
@@ -182,13 +234,14 @@ def main() -> int:
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": (f"stack_kernel: all {L} layers in one launch (with its clear kernel), "
+            "kernel": (f"stack1_kernel: all {L} layers in one launch (timed with its clear kernel), "
                        f"mean launch {launch_s * 1e6:.1f} us"),
             "achieved": round(kernel_gbps, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(kernel_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_detail": traffic_detail,
         },
     }
     if not args.no_cpu:
