@@ -67,6 +67,7 @@ struct Ptrs {
   uint32_t* masks;
   uint16_t* a_hi;
   uint16_t* a_lo;
+  float* ysh;  // shared expert's down projection [T][H] from the matrix-core path, or nullptr
 };
 
 __device__ __forceinline__ float silu_mul(float g, float v) { return g / (1.0f + expf(-g)) * v; }
@@ -147,6 +148,14 @@ __device__ __forceinline__ void row_stats(const Dims& d, const Ptrs& p, int t, i
     p.sg[t] = 1.0f / (1.0f + expf(-(r * gd)));
   }
 }
+
+}  // namespace
+}  // namespace moe
+
+#include "mfma.h"
+
+namespace moe {
+namespace {
 
 // ----------------------------------------------------------- route kernel
 template <int BITS, int CPL>
@@ -432,11 +441,16 @@ __global__ void __launch_bounds__(1024) down_kernel(Dims d, Ptrs p, int J) {
       const int e = s_units[u];
       const uint8_t* mat = p.layer + d.off_e0 + (int64_t)e * d.e_stride + d.off_e_down;
       MOE_BITS_CASES(d.ebits, B, down_unit<B, CPL, RD>(d, p, mat, d.I, j0, J, s_masks[u], -1, e, s_ids, s_D));
-    } else {
+    } else if (!p.ysh) {
       const uint8_t* mat = p.layer + d.off_shared + d.off_shared_down;
       MOE_BITS_CASES(d.sbits, B, down_unit<B, CPL, RD>(d, p, mat, d.Is, j0, J, all, d.k, -1, s_ids, s_D));
     }
   }
+  if (p.ysh)
+    for (int idx = tid; idx < d.T * J; idx += blockDim.x) {
+      const int t = idx / J, q = idx % J;
+      if (j0 + q < d.H) s_D[(t * (d.k + 1) + d.k) * J + q] = p.ysh[(int64_t)t * d.H + j0 + q];
+    }
   __syncthreads();
   for (int idx = tid; idx < d.T * J; idx += blockDim.x) {
     const int t = idx / J, q = idx % J, j = j0 + q;
@@ -450,13 +464,33 @@ __global__ void __launch_bounds__(1024) down_kernel(Dims d, Ptrs p, int J) {
   }
 }
 
+// Status word of a stack call that runs layer by layer: no wait can time out.
+__global__ void clear_status_kernel(uint32_t* status) { status[threadIdx.x] = 0u; }
+
 // ---------------------------------------------------------------- launch
 struct LayerPlan {
   Dims d;
   int cpl_h, cpl_i;
   int n_rt, n_st, tpu, g_grid;
   int J, RD, d_grid, d_threads;
+  // matrix-core router and shared expert (T > 8, 8-bit router and shared)
+  bool mfma;
+  int m_nt, m_ng_route, m_ng_down, m_rt, m_pt, m_down;
 };
+
+// MOE_MFMA=0 keeps every call on the vector-unit kernels (for comparison).
+bool mfma_enabled() {
+  static const bool on = [] {
+    const char* v = getenv("MOE_MFMA");
+    return !(v && v[0] == '0');
+  }();
+  return on;
+}
+
+int mfma_groups_per_load(int groups) {
+  const int gpw = (groups + kMfmaWaves - 1) / kMfmaWaves;
+  return gpw >= 8 ? 8 : gpw >= 4 ? 4 : 2;
+}
 
 LayerPlan make_plan(const moe_shape_t& s, const moe_layer_layout_t& L, int T) {
   LayerPlan P;
@@ -506,6 +540,16 @@ LayerPlan make_plan(const moe_shape_t& s, const moe_layer_layout_t& L, int T) {
   int nw = max_units + 1;
   if (nw > 16) nw = 16;
   P.d_threads = 64 * nw;
+  P.mfma = T >= kMfmaMinT && s.router_bits == 8 && s.shared_bits == 8 && mfma_enabled();
+  P.m_nt = T > 16 ? 2 : 1;
+  // groups in flight per wave, bounded by registers: 8 only with one token tile
+  P.m_ng_route = mfma_groups_per_load(s.hidden / kGroup);
+  if (P.m_nt == 2 && P.m_ng_route > 4) P.m_ng_route = 4;
+  P.m_ng_down = mfma_groups_per_load(s.shared_inter / kGroup);
+  if (P.m_ng_down > 4) P.m_ng_down = 4;
+  P.m_rt = (s.n_experts + 15) / 16;
+  P.m_pt = (s.shared_inter + 7) / 8;
+  P.m_down = (s.hidden + 15) / 16;
   return P;
 }
 
@@ -516,6 +560,23 @@ void launch_route(const LayerPlan& P, const Ptrs& p, hipStream_t st) {
 template <int CPL>
 void launch_expert(const LayerPlan& P, const Ptrs& p, hipStream_t st) {
   expert_kernel<CPL><<<P.g_grid, 256, 0, st>>>(P.d, p, P.tpu);
+}
+template <int NT>
+void launch_mfma(const LayerPlan& P, const Ptrs& p, hipStream_t st) {
+  switch (P.m_ng_route) {
+    case 8:
+      if constexpr (NT == 1) {
+        route_mfma_kernel<1, 8><<<P.m_rt + P.m_pt, kMfmaThreads, 0, st>>>(P.d, p, P.m_rt);
+        break;
+      }
+      [[fallthrough]];
+    case 4: route_mfma_kernel<NT, 4><<<P.m_rt + P.m_pt, kMfmaThreads, 0, st>>>(P.d, p, P.m_rt); break;
+    default: route_mfma_kernel<NT, 2><<<P.m_rt + P.m_pt, kMfmaThreads, 0, st>>>(P.d, p, P.m_rt); break;
+  }
+  switch (P.m_ng_down) {  // at most 4 groups in flight: two input parts
+    case 4: down_mfma_kernel<NT, 4><<<P.m_down, kMfmaThreads, 0, st>>>(P.d, p); break;
+    default: down_mfma_kernel<NT, 2><<<P.m_down, kMfmaThreads, 0, st>>>(P.d, p); break;
+  }
 }
 template <int CPL, int RD>
 void launch_down(const LayerPlan& P, const Ptrs& p, hipStream_t st) {
@@ -546,7 +607,14 @@ int32_t launch_layer(const LayerPlan& P, const WsMap& m, uint8_t* ws, const uint
   p.masks = (uint32_t*)(ws + m.masks);
   p.a_hi = (uint16_t*)(ws + m.a_hi);
   p.a_lo = (uint16_t*)(ws + m.a_lo);
-  MOE_CPL_CASES(P.cpl_h, C, launch_route<C>(P, p, st));
+  p.ysh = nullptr;
+  if (P.mfma) {
+    p.ysh = (float*)(ws + m.ysh);
+    if (P.m_nt == 2) launch_mfma<2>(P, p, st);
+    else launch_mfma<1>(P, p, st);
+  } else {
+    MOE_CPL_CASES(P.cpl_h, C, launch_route<C>(P, p, st));
+  }
   MOE_CPL_CASES(P.cpl_h, C, launch_expert<C>(P, p, st));
   // rows x chunks per lane <= 4 (make_plan)
   switch (P.cpl_i * 8 + P.RD) {
@@ -628,7 +696,7 @@ extern "C" int32_t moe_decode_stack(const moe_shape_t* shape, const void* const*
     hipError_t e = hipMemcpyAsync(h_trace_dev, h_in_dev, th * 2, hipMemcpyDeviceToDevice, st);
     if (e != hipSuccess) return set_error(MOE_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
   }
-  // One persistent kernel per up to 64 layers when the shape allows it: the
+  // One persistent kernel per up to 64 layers when the call allows it: the
   // one-row streaming kernel, else the general one. MOE_STACK_KERNEL selects
   // a path for comparison: 0 = per-layer kernels only, 1 = never the
   // streaming kernel. All paths give the same results bit for bit.
@@ -642,12 +710,14 @@ extern "C" int32_t moe_decode_stack(const moe_shape_t* shape, const void* const*
     if (rc != MOE_ERR_UNSUPPORTED) return rc;
     clear_error();
   }
-  if (stack_kernel_mode >= 1) {
+  // calls on the matrix-core path (T > 8) run layer by layer
+  if (stack_kernel_mode >= 1 && !P.mfma) {
     rc = launch_stack_persistent(*shape, L, m, (uint8_t*)ws_dev, layers_host, n_layers, T, h_in_dev, h_out_dev,
                                  ids_dev, w_dev, h_trace_dev, st);
     if (rc != MOE_ERR_UNSUPPORTED) return rc;
     clear_error();
   }
+  clear_status_kernel<<<1, 64, 0, st>>>((uint32_t*)((uint8_t*)ws_dev + m.status));
   const uint16_t* cur = h_in_dev;
   for (int l = 0; l < n_layers; ++l) {
     uint16_t* nxt;

@@ -55,6 +55,7 @@ struct WsMap {
   int64_t a_hi;         // bf16  [T][k+1][Imax]  SwiGLU activations, high part
   int64_t a_lo;         // bf16  [T][k+1][Imax]  low part: a = hi + lo to 16 significant bits
   int64_t hbuf;         // bf16  [2][T][H] ping-pong for stacks
+  int64_t ysh;          // float [T][H]  shared expert's down projection (matrix-core path)
   // stack kernel exchange buffers: 64-bit words = 32-bit payload | epoch << 32
   int64_t tg_h;         // u64 [T][H/2]       hidden state, two bf16 per word
   int64_t tg_logit;     // u64 [T][E]         raw router dot products

@@ -85,6 +85,7 @@ WsMap ws_map(const moe_shape_t& s, int T) {
   m.a_hi = take((int64_t)T * (k + 1) * imax * 2);
   m.a_lo = take((int64_t)T * (k + 1) * imax * 2);
   m.hbuf = take((int64_t)2 * T * s.hidden * 2);
+  m.ysh = take((int64_t)T * s.hidden * 4);
   m.tg_h = take((int64_t)T * (s.hidden / 2) * 8);
   m.tg_logit = take((int64_t)T * s.n_experts * 8);
   m.tg_rs = take((int64_t)T * 2 * 8);
