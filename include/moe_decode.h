@@ -165,6 +165,12 @@ int32_t moe_generate_rows(uint64_t seed_x, int32_t T, int32_t H, uint16_t* out_d
  *   ws_dev    : workspace of ws_bytes >= moe_workspace_bytes(shape, T),
  *               256-byte aligned; contents need no initialisation.
  * Calls that share one workspace must be ordered on one stream.
+ * Rows are independent. For T <= 8 (the verify batch of the PureDrive card,
+ * "How it works") row t of the result is bitwise equal to a one-row call on
+ * row t. For T > 8 with an 8-bit router and shared expert, those two run on
+ * the bf16 matrix cores (different fp32 summation order; rows agree with the
+ * one-row result to rounding, not bit for bit); MOE_MFMA=0 in the environment
+ * keeps them on the vector-unit kernels.
  */
 int32_t moe_decode_layer(const moe_shape_t* shape, const void* layer_dev, int32_t T, const uint16_t* h_in_dev,
                          uint16_t* h_out_dev, int32_t* ids_dev, float* w_dev, void* ws_dev, size_t ws_bytes,
@@ -175,8 +181,9 @@ int32_t moe_decode_layer(const moe_shape_t* shape, const void* layer_dev, int32_
  * h_{l+1} = bf16(layer_l(h_l)), h_out = h_{n_layers}. The host never waits
  * inside the stack. Each group of up to 64 layers runs as one kernel with one
  * workgroup per compute unit whose workgroups wait on each other's results
- * (bounded waits; see moe_stack_status); shapes it does not cover run as
- * three kernels per layer, which give the same results bit for bit.
+ * (bounded waits; see moe_stack_status); calls it does not cover run as
+ * kernels per layer (the same as moe_decode_layer), which give the same
+ * results bit for bit.
  *   layers_host : host array of n_layers device pointers to layer blocks
  *   ids_dev     : int32 [n_layers, T, k] or NULL; w_dev: float [n_layers, T, k] or NULL
  *   h_trace_dev : bf16 [n_layers + 1, T, H] (h_0 .. h_L) or NULL
