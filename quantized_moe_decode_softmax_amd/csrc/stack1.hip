@@ -24,21 +24,24 @@
 // cache line is polled by every compute unit. The activations, which every
 // workgroup reads in full, are not polled while they are produced: each
 // workgroup sets a ready flag once it has stored its share, a consumer waits
-// for all flags (one word per workgroup) and then reads the activations once,
-// still checking their tags.
+// for the flags of the workgroups that computed the slot it needs (one word
+// per workgroup) and then reads the activations once, still checking their
+// tags.
 //
 // Per layer and workgroup (8 waves, one workgroup per compute unit, as many
 // workgroups as the hidden state has slices of J rows):
 //   A  stream this workgroup's router rows and shared-expert row pairs; stage
 //      h_l in LDS; compute raw logits and shared activations; publish them
 //   R  wave 0: RMS factor and shared gate of the row, top-k of the logits,
-//      renormalised weights (every workgroup routes for itself)
+//      renormalised weights (every workgroup routes for itself), then an LDS
+//      flag releases the other waves; meanwhile the last wave computes the
+//      shared expert's down rows [j0, j0 + J), whose inputs came in phase A
 //   B  stream and compute this workgroup's range of routed row pairs
 //      (k experts x I pairs split evenly over the grid), then publish the
 //      activations and the ready flag; wait for every workgroup's flag and
 //      stage all k + 1 activation vectors in LDS
-//   C  down-projection rows [j0, j0 + J) of the k experts and the shared
-//      expert (weights streamed during B), combine in rank order, residual,
+//   C  down-projection rows [j0, j0 + J) of the k experts (weights streamed
+//      during B), combine in rank order with the shared rows, residual,
 //      bf16, publish the slice of h_{l+1}
 //
 // Buffer reuse: every workgroup publishes a slice of h in every layer. Logits,
@@ -407,6 +410,8 @@ struct Shared {
   int ids[kMaxTopK];
   float w[kMaxTopK];
   float r, sg;
+  uint32_t route_ep;  // epoch of the layer whose routing ids/w/r/sg hold
+  uint32_t logit_ep;  // epoch of the layer whose logits wave 0 has seen (so all phase A output exists)
   __attribute__((aligned(16))) uint8_t ring[kWaves][kRingBytes];
 };
 
@@ -516,37 +521,49 @@ __host__ __device__ __forceinline__ int down_task_rows(int J, int K, int bits) {
   while (n > rpw && seg_bytes(bits, K, n) > kHalf) n -= rpw;
   return n;
 }
+// C tasks: the routed experts' down rows of this workgroup's slice, slot by
+// slot (the shared expert's rows are computed during routing, see
+// shared_down_early)
 __device__ __forceinline__ int n_c_tasks(const Args& a, const Ctx& c) {
-  const int de = down_task_rows(c.J, c.I, c.ebits), ds = down_task_rows(c.J, c.Is, c.sbits);
-  return c.k * ((c.J + de - 1) / de) + (c.J + ds - 1) / ds;
+  const int de = down_task_rows(c.J, c.I, c.ebits);
+  return c.k * ((c.J + de - 1) / de);
 }
 __device__ __forceinline__ Task c_task(const Args& a, const Ctx& c, int i) {
-  const int de = down_task_rows(c.J, c.I, c.ebits), ds = down_task_rows(c.J, c.Is, c.sbits);
+  const int de = down_task_rows(c.J, c.I, c.ebits);
   const int tr = (c.J + de - 1) / de;
   const int j0 = blockIdx.x * c.J;
-  const int ts = (c.J + ds - 1) / ds;  // the shared expert's tasks come first: its
-                                       // activations exist since phase A
   Task t;
   t.kind = kDown;
   t.up = 0;
   t.rows_total = c.H;
-  if (i >= ts) {
-    i -= ts;
-    const int u = i / tr;
-    t.slot = u;
-    t.K = c.I;
-    t.bits = c.ebits;
-    t.mat = c.layer + c.off_e0 + (int64_t)S.ids[u] * c.e_stride + c.off_e_down;
-    t.r0 = j0 + (i % tr) * de;
-    t.n = min(de, min(j0 + c.J, c.H) - t.r0);
-  } else {
-    t.slot = c.k;
-    t.K = c.Is;
-    t.bits = c.sbits;
-    t.mat = c.layer + c.off_shared + c.off_shared_down;
-    t.r0 = j0 + i * ds;
-    t.n = min(ds, min(j0 + c.J, c.H) - t.r0);
-  }
+  const int u = i / tr;
+  t.slot = u;
+  t.K = c.I;
+  t.bits = c.ebits;
+  t.mat = c.layer + c.off_e0 + (int64_t)S.ids[u] * c.e_stride + c.off_e_down;
+  t.r0 = j0 + (i % tr) * de;
+  t.n = min(de, min(j0 + c.J, c.H) - t.r0);
+  t.bytes = task_bytes(t.bits, t.K, t.n, false);
+  return t;
+}
+// the shared expert's down rows of this workgroup's slice
+__device__ __forceinline__ int n_s_tasks(const Args& a, const Ctx& c) {
+  const int ds = down_task_rows(c.J, c.Is, c.sbits);
+  return (c.J + ds - 1) / ds;
+}
+__device__ __forceinline__ Task s_task(const Args& a, const Ctx& c, int i) {
+  const int ds = down_task_rows(c.J, c.Is, c.sbits);
+  const int j0 = blockIdx.x * c.J;
+  Task t;
+  t.kind = kDown;
+  t.up = 0;
+  t.rows_total = c.H;
+  t.slot = c.k;
+  t.K = c.Is;
+  t.bits = c.sbits;
+  t.mat = c.layer + c.off_shared + c.off_shared_down;
+  t.r0 = j0 + i * ds;
+  t.n = min(ds, min(j0 + c.J, c.H) - t.r0);
   t.bytes = task_bytes(t.bits, t.K, t.n, false);
   return t;
 }
@@ -696,6 +713,7 @@ __device__ __forceinline__ void route(const Args& a, const Ctx& c, const uint32_
 #pragma unroll
   for (int m = 0; m < M; ++m) want |= (c.lane + 64 * m < c.E ? 1u : 0u) << m;
   poll<M>(a.x_logit + c.cp * c.l_cs + c.lane, [](int m) { return (int64_t)64 * m; }, want, c.ep, rv, a.status);
+  *(volatile uint32_t*)&S.logit_ep = c.ep;
   int key[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) key[m] = c.lane + 64 * m < c.E ? fkey(r * __uint_as_float(rv[m])) : INT_MIN;
@@ -757,6 +775,40 @@ __device__ __forceinline__ void fetch_a(const Args& a, const Ctx& c, int slot) {
 // through the two ring halves, with the activation exchange between
 // KI, KS: routed and shared intermediate sizes when known at compile time
 // (0: run time); NV: activation elements per lane of a slot (>= imax / 64).
+// Waits until LDS word *p holds epoch (set by another wave of the workgroup).
+__device__ __forceinline__ void wait_lds_epoch(const uint32_t* p, uint32_t epoch, uint32_t* status) {
+  uint32_t spins = 0;
+  while (*(volatile const uint32_t*)p != epoch)
+    if (give_up(spins, status)) break;
+  asm volatile("" ::: "memory");
+}
+
+// The shared expert's down rows of this workgroup's slice, computed by the
+// last wave while wave 0 routes: their inputs were published in phase A, so
+// they need only the other workgroups' phase A, not the routing. The wave
+// reads them once wave 0 has seen every logit (published after the shared
+// activations), rather than polling them while they are produced.
+template <int CPL_I, int SB, int KS, int NV>
+__device__ __forceinline__ void shared_down_early(const Args& a, const Ctx& c) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's phase A reads of its ring are done
+  const uint32_t base = lds_addr(S.ring[c.wave]);
+  const int ns = n_s_tasks(a, c);
+  for (int i0 = 0; i0 < ns; i0 += 2) {
+    const int i1 = min(ns, i0 + 2);
+    for (int i = i0; i < i1; ++i) dma_task(s_task(a, c, i), base + (i - i0) * kHalf);
+    if (i0 == 0) {
+      wait_lds_epoch(&S.logit_ep, c.ep, a.status);
+      fetch_a<NV>(a, c, c.k);
+    }
+    wait_vm(0);
+    for (int i = i0; i < i1; ++i) {
+      const Task t = s_task(a, c, i);
+      MOE_T1_BITS(SB, c.sbits, B, down_rows<B, CPL_I, KS>(a, c, t, S.ring[c.wave] + (i - i0) * kHalf));
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // ring reads done before a refill
+  }
+}
+
 template <int CPL_H, int CPL_I, int EB, int SB, int KI, int KS, int NV>
 __device__ __forceinline__ void phases_bc(const Args& a, const Ctx& c) {
   const int nb = n_b_tasks<CPL_H, CPL_I>(a, c), nc = n_c_tasks(a, c);
@@ -812,10 +864,12 @@ __device__ __forceinline__ void phases_bc(const Args& a, const Ctx& c) {
           h_lane<B, CPL_H>(S.h, c.H, c.li_h, c.lpr_h, x);
           pair_rows<CPL_H, CPL_I, B>(a, c, t, buf, x, S.r, t.slot * c.I + t.r0 - f0);
         });
-      } else if (t.slot < c.k) {
-        MOE_T1_BITS(EB, c.ebits, B, down_rows<B, CPL_I, KI>(a, c, t, buf));
+        if (j + 1 == mb) {  // the wave's last routed pair: publish without waiting for the next batch
+          publish_a(a, c);
+          exchanged = true;
+        }
       } else {
-        MOE_T1_BITS(SB, c.sbits, B, down_rows<B, CPL_I, KS>(a, c, t, buf));
+        MOE_T1_BITS(EB, c.ebits, B, down_rows<B, CPL_I, KI>(a, c, t, buf));
       }
       off += t.bytes;
     }
@@ -939,6 +993,7 @@ __global__ void __launch_bounds__(kThreads) stack1_kernel(Args a) {
   c.li_h = c.lane % c.lpr_h;
   c.sr_h = c.lane / c.lpr_h;
   c.cp = blockIdx.x % c.n_copy;
+  if (threadIdx.x == 0) S.route_ep = S.logit_ep = 0u;  // ordered before their readers by the first barrier below
   for (int l = 0; l < a.n_layers; ++l) {
     c.layer = a.layers[l];
     c.ep = (uint32_t)l + 1;
@@ -973,9 +1028,13 @@ __global__ void __launch_bounds__(kThreads) stack1_kernel(Args a) {
         default: MOE_T1_RBITS(RB, c.rbits, B, route<CPL_H, B, 8, SH::k>(a, c, gvn)); break;
       }
     }
-  }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // routing stored before its flag
+      *(volatile uint32_t*)&S.route_ep = c.ep;
+    } else if (c.wave == kWaves - 1) {
+      shared_down_early<CPL_I, SB, SH::KS, SH::NV>(a, c);
+    }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // phase A ring reads done
-    lds_barrier();
+    wait_lds_epoch(&S.route_ep, c.ep, a.status);  // wave 0's routing is in LDS
     if (blockIdx.x == 0 && threadIdx.x < c.k) {
       if (a.ids_out) a.ids_out[(int64_t)l * c.k + threadIdx.x] = S.ids[threadIdx.x];
       if (a.w_out) a.w_out[(int64_t)l * c.k + threadIdx.x] = S.w[threadIdx.x];
