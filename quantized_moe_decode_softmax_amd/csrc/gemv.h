@@ -671,12 +671,10 @@ __device__ __forceinline__ void topk_select(int (&key)[M], int k, int& lane_id, 
     }
   // k rounds of wave max; the selected logits are wave-uniform, lane i keeps
   // round i's (id, logit) so no per-lane array is ever indexed by the lane
-  float sel[KMAX];
-  float my_sel = -INFINITY;
+  float my_sel = -INFINITY, top = 0.f;
   lane_id = 0;
 #pragma unroll
   for (int i = 0; i < KMAX; ++i) {
-    sel[i] = -INFINITY;
     if (i < k) {
       const int mx = wave_max_i(key[0]);
       const unsigned long long b = __ballot(key[0] == mx);
@@ -695,20 +693,20 @@ __device__ __forceinline__ void topk_select(int (&key)[M], int k, int& lane_id, 
         key[M - 1] = INT_MIN;
         idx[M - 1] = INT_MAX;
       }
-      sel[i] = key_f(mx);
+      const float v = key_f(mx);
+      if (i == 0) top = v;
       if (lane == i) {
         lane_id = id;
-        my_sel = sel[i];
+        my_sel = v;
       }
     }
   }
-  // renormalised softmax over the k selected logits, max first
-  const float mx = sel[0];
-  float sum = 0.f;
-#pragma unroll
-  for (int i = 0; i < KMAX; ++i)
-    if (i < k) sum += expf(sel[i] - mx);  // uniform branch
-  lane_w = lane < k ? expf(my_sel - mx) / sum : 0.f;
+  // renormalised softmax over the k selected logits, the largest subtracted:
+  // one exponential per lane, summed over lanes 0..k-1 (k <= 16, one row of
+  // 16 lanes) in a fixed tree
+  const float e = lane < k ? expf(my_sel - top) : 0.f;
+  const float sum = reduce_row(e, 16);
+  lane_w = lane < k ? e / sum : 0.f;
 }
 
 // Top-k of one token row on one wave: logits lam_src[0..E) scaled by

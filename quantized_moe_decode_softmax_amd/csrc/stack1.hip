@@ -37,9 +37,10 @@
 //      flag releases the other waves; meanwhile the last wave computes the
 //      shared expert's down rows [j0, j0 + J), whose inputs came in phase A
 //   B  stream and compute this workgroup's range of routed row pairs
-//      (k experts x I pairs split evenly over the grid), then publish the
-//      activations and the ready flag; wait for every workgroup's flag and
-//      stage all k + 1 activation vectors in LDS
+//      (k experts x I pairs split evenly over the grid), storing each
+//      activation as it is computed, then set the workgroup's ready flag;
+//      each wave then waits for the flags of the workgroups that computed
+//      the slot of its down task and reads that activation vector into LDS
 //   C  down-projection rows [j0, j0 + J) of the k experts (weights streamed
 //      during B), combine in rank order with the shared rows, residual,
 //      bf16, publish the slice of h_{l+1}
@@ -77,7 +78,6 @@ constexpr uint32_t kSpinLimit = 1u << 21;
 constexpr int kMaxWG = 512;
 constexpr int kMaxH = 4096;
 constexpr int kMaxAWords = 12288;  // (k + 1) * imax
-constexpr int kMaxLocalA = 256;    // routed activations one workgroup computes per layer
 
 struct Args {
   int H, E, I, Is, k, imax;
@@ -405,7 +405,6 @@ __device__ __forceinline__ int dma_task(const Task& t, uint32_t dst) {
 struct Shared {
   uint32_t h[kMaxH / 2];         // h_l, bf16 pairs
   uint32_t a[kMaxAWords];        // activation vectors of the k + 1 slots, hi | lo << 16
-  uint32_t la[kMaxLocalA];       // routed activations computed here (split form)
   float D[(kMaxTopK + 1) * 16];  // down-projection outputs [slot][J]
   int ids[kMaxTopK];
   float w[kMaxTopK];
@@ -591,7 +590,7 @@ __device__ __forceinline__ void router_row(const Args& a, const Ctx& c, const Ta
 // (shared expert), else the routed rows' factor
 template <int CPL_H, int CPL_I, int BITS>
 __device__ __forceinline__ void pair_rows(const Args& a, const Ctx& c, const Task& t, const uint8_t* buf,
-                                        const XLane<BITS, CPL_H>& x, float r, int local0) {
+                                        const XLane<BITS, CPL_H>& x, float r) {
   const int cb = code_bytes(BITS, c.H), sbw = c.H >> 6;
   const int half = t.bytes / 2;
   float pg = 0.f, pu = 0.f;
@@ -607,11 +606,11 @@ __device__ __forceinline__ void pair_rows(const Args& a, const Ctx& c, const Tas
   const float gv = reduce_row(pg, c.lpr_h) * rr;
   const float uv = reduce_row(pu, c.lpr_h) * rr;
   if (c.sr_h < t.n && c.li_h == c.lpr_h - 1) {
-    const uint32_t w = split_a(silu_mul(gv, uv));
-    if (t.kind == kSharedPair)
-      st_copies(a.x_a + (int64_t)c.k * c.imax + a_word(t.r0 + c.sr_h, c.imax), c.a_cs, c.n_copy, w, c.ep);
-    else
-      S.la[local0 + c.sr_h] = w;  // published with the flag
+    // stored at once (a routed pair's ready flag follows after the
+    // workgroup's last pair, by when these stores have long completed)
+    const int slot = t.kind == kSharedPair ? c.k : t.slot;
+    st_copies(a.x_a + (int64_t)slot * c.imax + a_word(t.r0 + c.sr_h, c.imax), c.a_cs, c.n_copy,
+              split_a(silu_mul(gv, uv)), c.ep);
   }
 }
 
@@ -660,7 +659,7 @@ __device__ __forceinline__ void phase_a_compute(const Args& a, const Ctx& c) {
       MOE_T1_BITS(SB, c.sbits, B, {
         XLane<B, CPL_H> x;
         h_lane<B, CPL_H>(S.h, c.H, c.li_h, c.lpr_h, x);
-        pair_rows<CPL_H, CPL_I, B>(a, c, t, buf, x, -1.f, 0);
+        pair_rows<CPL_H, CPL_I, B>(a, c, t, buf, x, -1.f);
       });
     }
     off += t.bytes;
@@ -730,41 +729,56 @@ __device__ __forceinline__ void route(const Args& a, const Ctx& c, const uint32_
   }
 }
 
-// ---- activations: publish this workgroup's routed ones and its ready flag
-// (every wave calls this once, after its B tasks)
+// ---- activations: this workgroup's ready flag, once every wave has stored
+// its routed activations (every wave calls this once, after its B tasks)
 __device__ __forceinline__ void publish_a(const Args& a, const Ctx& c) {
-  lds_barrier();  // S.la complete
-  const int f0 = blockIdx.x * c.pb, f1 = min(c.k * c.I, f0 + c.pb);
-  if (c.wave == 0) {
-    for (int f = f0 + c.lane; f < f1; f += 64) {
-      const int u = f / c.I, i = f % c.I;
-      st_copies(a.x_a + (int64_t)u * c.imax + a_word(i, c.imax), c.a_cs, c.n_copy, S.la[f - f0], c.ep);
-    }
-    if (c.lane == 0) st_copies(a.x_flag + blockIdx.x, 512, c.n_copy, 1u, c.ep);
-  }
+  lds_barrier();
+  if (c.wave == 0 && c.lane == 0) st_copies(a.x_flag + blockIdx.x, 512, c.n_copy, 1u, c.ep);
 }
 
 // ---- the activation vector of one slot into S.a (one wave): for a routed
-// slot first the ready flags of the workgroups that computed it (those whose
-// pair ranges meet it), then every element in one round of loads; the
-// shared slot's activations were stored in phase A and are read directly.
+// slot one read of every element, then the ready flags of the workgroups that
+// computed it (those whose pair ranges meet it), then the elements whose tags
+// were not yet current, until they are; the shared slot's activations were
+// stored in phase A and are polled directly.
 // NV >= K / 64: elements per lane.
 template <int NV>
 __device__ __forceinline__ void fetch_a(const Args& a, const Ctx& c, int slot) {
   const int K = slot < c.k ? c.I : c.Is;
-  if (slot < c.k) {
-    const int w0 = slot * c.I / c.pb, w1 = ((slot + 1) * c.I - 1) / c.pb;
-    uint32_t v[2];
-    const uint32_t want = (w0 + c.lane <= w1 ? 1u : 0u) | (w0 + c.lane + 64 <= w1 ? 2u : 0u);
-    poll<2>(a.x_flag + c.cp * 512 + w0 + c.lane, [](int m) { return (int64_t)64 * m; }, want, c.ep, v, a.status);
-  }
   const uint64_t* src = a.x_a + c.cp * c.a_cs + (int64_t)slot * c.imax;
-  uint32_t v[NV];
+  const int imax = c.imax, lane = c.lane;
+  auto off = [imax, lane](int j) { return (int64_t)a_word(lane + 64 * j, imax); };
   uint32_t want = 0u;
 #pragma unroll
   for (int j = 0; j < NV; ++j) want |= (c.lane + 64 * j < K ? 1u : 0u) << j;
-  const int imax = c.imax, lane = c.lane;
-  poll<NV>(src, [imax, lane](int j) { return (int64_t)a_word(lane + 64 * j, imax); }, want, c.ep, v, a.status);
+  uint32_t v[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) v[j] = 0u;
+  uint32_t pending = want;
+  if (slot < c.k) {
+    // one read of the slot's words before the flags: most were stored as
+    // their pairs were computed, so only the late ones are read again below
+    uint64_t sv[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) sv[j] = (want >> j & 1u) ? ld_tag(src + off(j)) : 0ull;
+    const int w0 = slot * c.I / c.pb, w1 = ((slot + 1) * c.I - 1) / c.pb;
+    uint32_t fv[2];
+    const uint32_t fwant = (w0 + c.lane <= w1 ? 1u : 0u) | (w0 + c.lane + 64 <= w1 ? 2u : 0u);
+    poll<2>(a.x_flag + c.cp * 512 + w0 + c.lane, [](int m) { return (int64_t)64 * m; }, fwant, c.ep, fv, a.status);
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+      if ((want >> j & 1u) && (uint32_t)(sv[j] >> 32) == c.ep) {
+        v[j] = (uint32_t)sv[j];
+        pending &= ~(1u << j);
+      }
+  }
+  if (pending) {
+    uint32_t pv[NV];
+    poll<NV>(src, off, pending, c.ep, pv, a.status);
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+      if (pending >> j & 1u) v[j] = pv[j];
+  }
   uint32_t* dst = S.a + slot * c.imax;
 #pragma unroll
   for (int j = 0; j < NV; ++j)
@@ -858,11 +872,10 @@ __device__ __forceinline__ void phases_bc(const Args& a, const Ctx& c) {
       }
       const uint8_t* buf = S.ring[c.wave] + h * kHalf + off;
       if (t.kind == kRoutedPair) {
-        const int f0 = blockIdx.x * c.pb;
         MOE_T1_BITS(EB, c.ebits, B, {
           XLane<B, CPL_H> x;
           h_lane<B, CPL_H>(S.h, c.H, c.li_h, c.lpr_h, x);
-          pair_rows<CPL_H, CPL_I, B>(a, c, t, buf, x, S.r, t.slot * c.I + t.r0 - f0);
+          pair_rows<CPL_H, CPL_I, B>(a, c, t, buf, x, S.r);
         });
         if (j + 1 == mb) {  // the wave's last routed pair: publish without waiting for the next batch
           publish_a(a, c);
@@ -1094,7 +1107,6 @@ int32_t launch_stack_t1(const moe_shape_t& s, const moe_layer_layout_t& L, const
   const int a_tasks = (ra + rpw_h - 1) / rpw_h + (sa + rpw_h - 1) / rpw_h;
   if ((a_tasks + kWaves - 1) / kWaves * std::max(router_task, shared_task) > kRingBytes) return MOE_ERR_UNSUPPORTED;
   const int pb = (s.top_k * s.inter + nwg - 1) / nwg;
-  if (pb > kMaxLocalA) return MOE_ERR_UNSUPPORTED;
   // a slot's activations: at most 32 per lane, from at most 128 workgroups
   if (imax > 32 * 64 || s.inter / pb + 2 > 128) return MOE_ERR_UNSUPPORTED;
 
