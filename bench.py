@@ -47,7 +47,7 @@ KERNEL_SOURCES = ["stack1.hip", "gemv.h", "device_common.h"]  # the stack kernel
 # 256 MiB device copy measured the same way. Keyed by workload; valid only
 # for the kernel sources whose hash is stored with it.
 TRAFFIC = {
-    "a3b": {"src_hash": "9768287fa41f83f4", "fetch_bytes": 997_120_343, "write_bytes": 55_063_859},
+    "a3b": {"src_hash": "42a72c16795637d5", "fetch_bytes": 993_753_370, "write_bytes": 55_063_702},
 }
 
 
@@ -59,6 +59,16 @@ def kernel_source_hash() -> str:
         with open(os.path.join(ROOT, "quantized_moe_decode_softmax_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def kernel_path(w) -> str:
+    """What one moe_decode_stack call launches for this workload."""
+    if w.T == 1:
+        return f"stack1_kernel: all {w.n_layers} layers in one launch (timed with its clear kernel)"
+    if w.T > 8 and w.router_bits == 8 and w.shared_bits == 8:
+        return (f"per-layer kernels: route_mfma, down_mfma, expert, down per layer ({w.n_layers} layers, "
+                f"timed together)")
+    return f"stack_kernel: all {w.n_layers} layers in one launch (timed with its clear kernel)"
 
 
 def copy_probe(mib: int) -> int:
@@ -234,8 +244,7 @@ def main() -> int:
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": (f"stack1_kernel: all {L} layers in one launch (timed with its clear kernel), "
-                       f"mean launch {launch_s * 1e6:.1f} us"),
+            "kernel": f"{kernel_path(w)}, mean call {launch_s * 1e6:.1f} us",
             "achieved": round(kernel_gbps, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

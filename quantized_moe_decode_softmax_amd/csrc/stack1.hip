@@ -756,21 +756,26 @@ __device__ __forceinline__ void fetch_a(const Args& a, const Ctx& c, int slot) {
   for (int j = 0; j < NV; ++j) v[j] = 0u;
   uint32_t pending = want;
   if (slot < c.k) {
-    // one read of the slot's words before the flags: most were stored as
-    // their pairs were computed, so only the late ones are read again below
-    uint64_t sv[NV];
+    // one read of the slot's words before the flags (up to 8 per lane; more
+    // would take registers the kernel lacks): most were stored as their pairs
+    // were computed, so only the late ones are read again below
+    uint64_t sv[NV <= 8 ? NV : 1];
+    if constexpr (NV <= 8) {
 #pragma unroll
-    for (int j = 0; j < NV; ++j) sv[j] = (want >> j & 1u) ? ld_tag(src + off(j)) : 0ull;
+      for (int j = 0; j < NV; ++j) sv[j] = (want >> j & 1u) ? ld_tag(src + off(j)) : 0ull;
+    }
     const int w0 = slot * c.I / c.pb, w1 = ((slot + 1) * c.I - 1) / c.pb;
     uint32_t fv[2];
     const uint32_t fwant = (w0 + c.lane <= w1 ? 1u : 0u) | (w0 + c.lane + 64 <= w1 ? 2u : 0u);
     poll<2>(a.x_flag + c.cp * 512 + w0 + c.lane, [](int m) { return (int64_t)64 * m; }, fwant, c.ep, fv, a.status);
+    if constexpr (NV <= 8) {
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
-      if ((want >> j & 1u) && (uint32_t)(sv[j] >> 32) == c.ep) {
-        v[j] = (uint32_t)sv[j];
-        pending &= ~(1u << j);
-      }
+      for (int j = 0; j < NV; ++j)
+        if ((want >> j & 1u) && (uint32_t)(sv[j] >> 32) == c.ep) {
+          v[j] = (uint32_t)sv[j];
+          pending &= ~(1u << j);
+        }
+    }
   }
   if (pending) {
     uint32_t pv[NV];
