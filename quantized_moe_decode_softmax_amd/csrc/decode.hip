@@ -293,68 +293,65 @@ __global__ void __launch_bounds__(64, 2) route_kernel(Dims d, Ptrs p, int n_rt) 
   }
 }
 
+// ---------------------------------------------------------- select kernel
+// Routing of the call, once: top-k of every token row (row t on wave t % 16),
+// the renormalised weights, and the ascending list of experts used by any
+// row with the mask of rows using each. One workgroup of 1024 threads.
+__global__ void __launch_bounds__(1024) select_kernel(Dims d, Ptrs p) {
+  __shared__ uint32_t s_emask[kMaxExperts];
+  __shared__ int s_wcnt[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < d.E; e += 1024) s_emask[e] = 0u;
+  __syncthreads();
+  for (int t = wave; t < d.T; t += 16) {
+    int my_id;
+    float my_w, r;
+    wave_topk(p.raw + (int64_t)t * d.E, p.rinv + t, d.E, d.k, my_id, my_w, r);
+    if (lane < d.k) {  // lane i holds entry i
+      const int i = t * d.k + lane;
+      p.ids[i] = my_id;
+      p.wts[i] = my_w;
+      if (p.ids_out) p.ids_out[i] = my_id;
+      if (p.w_out) p.w_out[i] = my_w;
+      atomicOr(&s_emask[my_id], 1u << t);  // OR: the result does not depend on the order
+    }
+  }
+  __syncthreads();
+  // experts used by any row, ascending (E <= 1024: one per thread)
+  const bool used = tid < d.E && s_emask[tid] != 0u;
+  const unsigned long long bal = __ballot(used);
+  if (lane == 0) s_wcnt[wave] = __popcll(bal);
+  __syncthreads();
+  int off = __popcll(bal & ((1ull << lane) - 1ull));
+  int n = 0;
+  for (int w = 0; w < 16; ++w) {
+    if (w < wave) off += s_wcnt[w];
+    n += s_wcnt[w];
+  }
+  if (used) {
+    p.units[1 + off] = tid;
+    p.masks[off] = s_emask[tid];
+  }
+  if (tid == 0) p.units[0] = n;
+}
+
 // ---------------------------------------------------------- expert kernel
 template <int CPL>
 __global__ void __launch_bounds__(256, 2) expert_kernel(Dims d, Ptrs p, int tasks_per_unit) {
   __shared__ int s_ids[kMaxT * kMaxTopK];
-  __shared__ float s_w[kMaxT * kMaxTopK];
   __shared__ float s_r[kMaxT];
-  __shared__ uint32_t s_emask[kMaxExperts];
   __shared__ int s_units[kMaxUnits];
   __shared__ uint32_t s_masks[kMaxUnits];
-  __shared__ int s_wcnt[4];
-  __shared__ int s_nunits;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < d.E; e += 256) s_emask[e] = 0u;
-  __syncthreads();
-  // routing of every token row (row t on wave t % 4)
-  for (int t = wave; t < d.T; t += 4) {
-    int my_id;
-    float my_w, r;
-    wave_topk(p.raw + (int64_t)t * d.E, p.rinv + t, d.E, d.k, my_id, my_w, r);
-    // lane i publishes entry i
-    if (lane < d.k) {
-      s_ids[t * kMaxTopK + lane] = my_id;
-      s_w[t * kMaxTopK + lane] = my_w;
-      atomicOr(&s_emask[my_id], 1u << t);
-    }
-    if (lane == 0) s_r[t] = r;
+  // the call's routing (select_kernel), staged once
+  const int n_units = p.units[0];
+  for (int i = tid; i < d.T * d.k; i += 256) s_ids[(i / d.k) * kMaxTopK + i % d.k] = p.ids[i];
+  for (int t = tid; t < d.T; t += 256) s_r[t] = p.rinv[t];
+  for (int u = tid; u < n_units; u += 256) {
+    s_units[u] = p.units[1 + u];
+    s_masks[u] = p.masks[u];
   }
   __syncthreads();
-  // experts used by any row, ascending
-  int base = 0;
-  for (int e0 = 0; e0 < d.E; e0 += 256) {
-    const int e = e0 + tid;
-    const bool used = e < d.E && s_emask[e] != 0u;
-    const unsigned long long bal = __ballot(used);
-    const int before = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) s_wcnt[wave] = __popcll(bal);
-    __syncthreads();
-    int off = base;
-    for (int w = 0; w < wave; ++w) off += s_wcnt[w];
-    if (used) {
-      s_units[off + before] = e;
-      s_masks[off + before] = s_emask[e];
-    }
-    base += s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
-    __syncthreads();
-  }
-  const int n_units = base;
-  if (blockIdx.x == 0) {
-    for (int i = tid; i < d.T * d.k; i += 256) {
-      const int t = i / d.k, j = i % d.k;
-      p.ids[i] = s_ids[t * kMaxTopK + j];
-      p.wts[i] = s_w[t * kMaxTopK + j];
-      if (p.ids_out) p.ids_out[i] = s_ids[t * kMaxTopK + j];
-      if (p.w_out) p.w_out[i] = s_w[t * kMaxTopK + j];
-    }
-    for (int u = tid; u < n_units; u += 256) {
-      p.units[1 + u] = s_units[u];
-      p.masks[u] = s_masks[u];
-    }
-    if (tid == 0) p.units[0] = n_units;
-  }
-  (void)s_nunits;
   // SwiGLU tasks: (unit, block of row pairs)
   const int lpr = lanes_per_row(d.H), rpw = 64 / lpr, sr = lane / lpr, li = lane % lpr;
   constexpr int RP = TaskRows<CPL>::R / 2;
@@ -559,6 +556,7 @@ void launch_route(const LayerPlan& P, const Ptrs& p, hipStream_t st) {
 }
 template <int CPL>
 void launch_expert(const LayerPlan& P, const Ptrs& p, hipStream_t st) {
+  select_kernel<<<1, 1024, 0, st>>>(P.d, p);
   expert_kernel<CPL><<<P.g_grid, 256, 0, st>>>(P.d, p, P.tpu);
 }
 template <int NT>
