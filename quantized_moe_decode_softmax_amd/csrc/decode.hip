@@ -115,6 +115,13 @@ template <int CPL>
 struct TaskRows {
   static constexpr int R = CPL >= 2 ? 2 : 4;  // rows loaded per lane group
 };
+// row pairs per lane group of one routed-expert task: more than the route
+// kernel's, so that a token row's arranged input serves several pairs and a
+// wave has more weight bytes in flight per task
+template <int CPL>
+struct ExpertPairs {
+  static constexpr int RP = CPL >= 4 ? 1 : 2;
+};
 
 // RMS factor and shared-expert gate of token row t (written once per call),
 // from the lane's arranged x chunks: ss = sum of squares, gate = gvec . h with
@@ -215,11 +222,10 @@ __device__ __forceinline__ void router_task(const Dims& d, const Ptrs& p, int ta
 
 // SwiGLU rows of one expert block (gate rows [0, I), up rows at +off_up):
 // task covers pairs i = i0 + sr + rpw * r. rowmask: token rows using it.
-template <int BITS, int CPL>
+template <int BITS, int CPL, int RP>
 __device__ __forceinline__ void swiglu_task(const Dims& d, const Ptrs& p, const uint8_t* blk, int64_t off_up, int I, int i0,
                             uint32_t rowmask, int slot_fixed, int e, const int* s_ids, const float* rinv, int li,
                             int lpr, int sr, int rpw) {
-  constexpr int RP = TaskRows<CPL>::R / 2;  // pairs per lane group
   constexpr int R = 2 * RP;
   const int64_t rb = row_bytes(BITS, d.H);
   const int64_t cb = matrix_codes_bytes(BITS, I, d.H);
@@ -288,7 +294,7 @@ __global__ void __launch_bounds__(64, 2) route_kernel(Dims d, Ptrs p, int n_rt) 
     const int i0 = (task - n_rt) * RP * rpw;
     const uint32_t all = d.T >= 32 ? 0xFFFFFFFFu : ((1u << d.T) - 1u);
     MOE_BITS_CASES(d.sbits, B,
-                   swiglu_task<B, CPL>(d, p, p.layer + d.off_shared, d.off_shared_up, d.Is, i0, all, d.k, -1, nullptr,
+                   swiglu_task<B, CPL, RP>(d, p, p.layer + d.off_shared, d.off_shared_up, d.Is, i0, all, d.k, -1, nullptr,
                                        nullptr, li, lpr, sr, rpw));
   }
 }
@@ -354,7 +360,7 @@ __global__ void __launch_bounds__(256, 2) expert_kernel(Dims d, Ptrs p, int task
   __syncthreads();
   // SwiGLU tasks: (unit, block of row pairs)
   const int lpr = lanes_per_row(d.H), rpw = 64 / lpr, sr = lane / lpr, li = lane % lpr;
-  constexpr int RP = TaskRows<CPL>::R / 2;
+  constexpr int RP = ExpertPairs<CPL>::RP;
   const int n_tasks = n_units * tasks_per_unit;
   for (int task = blockIdx.x * 4 + wave; task < n_tasks; task += gridDim.x * 4) {
     const int u = task / tasks_per_unit;
@@ -362,7 +368,7 @@ __global__ void __launch_bounds__(256, 2) expert_kernel(Dims d, Ptrs p, int task
     const int e = s_units[u];
     const uint8_t* blk = p.layer + d.off_e0 + (int64_t)e * d.e_stride;
     MOE_BITS_CASES(d.ebits, B,
-                   swiglu_task<B, CPL>(d, p, blk, d.off_e_up, d.I, i0, s_masks[u], -1, e, s_ids, s_r, li, lpr, sr,
+                   swiglu_task<B, CPL, RP>(d, p, blk, d.off_e_up, d.I, i0, s_masks[u], -1, e, s_ids, s_r, li, lpr, sr,
                                        rpw));
   }
 }
@@ -518,7 +524,8 @@ LayerPlan make_plan(const moe_shape_t& s, const moe_layer_layout_t& L, int T) {
   const int R = P.cpl_h >= 2 ? 2 : 4;
   P.n_rt = (d.E + R * rpw_h - 1) / (R * rpw_h);
   P.n_st = (d.Is + (R / 2) * rpw_h - 1) / ((R / 2) * rpw_h);
-  P.tpu = (d.I + (R / 2) * rpw_h - 1) / ((R / 2) * rpw_h);
+  const int rpe = P.cpl_h >= 4 ? ExpertPairs<4>::RP : P.cpl_h == 2 ? ExpertPairs<2>::RP : ExpertPairs<1>::RP;
+  P.tpu = (d.I + rpe * rpw_h - 1) / (rpe * rpw_h);
   const int max_units = T * d.k < d.E ? T * d.k : d.E;
   const int waves = max_units * P.tpu;
   P.g_grid = (waves + 3) / 4;
