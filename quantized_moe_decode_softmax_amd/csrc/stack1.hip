@@ -34,15 +34,17 @@
 //      h_l in LDS; compute raw logits and shared activations; publish them
 //   R  wave 0: RMS factor and shared gate of the row, top-k of the logits,
 //      renormalised weights (every workgroup routes for itself), then an LDS
-//      flag releases the other waves; meanwhile the last wave computes the
-//      shared expert's down rows [j0, j0 + J), whose inputs came in phase A
+//      flag releases the other waves; meanwhile the last wave loads the
+//      shared expert's down rows [j0, j0 + J) and their inputs (published in
+//      phase A) into LDS
 //   B  stream and compute this workgroup's range of routed row pairs
 //      (k experts x I pairs split evenly over the grid), storing each
 //      activation as it is computed, then set the workgroup's ready flag;
 //      each wave then waits for the flags of the workgroups that computed
 //      the slot of its down task and reads that activation vector into LDS
-//   C  down-projection rows [j0, j0 + J) of the k experts (weights streamed
-//      during B), combine in rank order with the shared rows, residual,
+//   C  the shared expert's down rows (one task per wave, while the ready
+//      flags are awaited), the down-projection rows [j0, j0 + J) of the k
+//      experts (weights streamed during B), combine in rank order, residual,
 //      bf16, publish the slice of h_{l+1}
 //
 // Buffer reuse: every workgroup publishes a slice of h in every layer. Logits,
@@ -412,6 +414,7 @@ struct Shared {
   uint32_t route_ep;  // epoch of the layer whose routing ids/w/r/sg hold
   uint32_t logit_ep;  // epoch of the layer whose logits wave 0 has seen (so all phase A output exists)
   __attribute__((aligned(16))) uint8_t ring[kWaves][kRingBytes];
+  __attribute__((aligned(16))) uint8_t sd[kRingBytes];  // the shared expert's down rows of the slice
 };
 
 // ------------------------------------------------------------- the kernel
@@ -521,8 +524,8 @@ __host__ __device__ __forceinline__ int down_task_rows(int J, int K, int bits) {
   return n;
 }
 // C tasks: the routed experts' down rows of this workgroup's slice, slot by
-// slot (the shared expert's rows are computed during routing, see
-// shared_down_early)
+// slot (the shared expert's rows are computed separately, see
+// shared_down_fetch)
 __device__ __forceinline__ int n_c_tasks(const Args& a, const Ctx& c) {
   const int de = down_task_rows(c.J, c.I, c.ebits);
   return c.k * ((c.J + de - 1) / de);
@@ -546,12 +549,17 @@ __device__ __forceinline__ Task c_task(const Args& a, const Ctx& c, int i) {
   return t;
 }
 // the shared expert's down rows of this workgroup's slice
+// (one pass of a wave's row groups each, so that the waves share them)
+__host__ __device__ __forceinline__ int s_task_rows(int J, int Is) {
+  const int rpw = 64 / lanes_per_row(Is);
+  return rpw < J ? rpw : J;
+}
 __device__ __forceinline__ int n_s_tasks(const Args& a, const Ctx& c) {
-  const int ds = down_task_rows(c.J, c.Is, c.sbits);
+  const int ds = s_task_rows(c.J, c.Is);
   return (c.J + ds - 1) / ds;
 }
 __device__ __forceinline__ Task s_task(const Args& a, const Ctx& c, int i) {
-  const int ds = down_task_rows(c.J, c.Is, c.sbits);
+  const int ds = s_task_rows(c.J, c.Is);
   const int j0 = blockIdx.x * c.J;
   Task t;
   t.kind = kDown;
@@ -802,29 +810,28 @@ __device__ __forceinline__ void wait_lds_epoch(const uint32_t* p, uint32_t epoch
   asm volatile("" ::: "memory");
 }
 
-// The shared expert's down rows of this workgroup's slice, computed by the
-// last wave while wave 0 routes: their inputs were published in phase A, so
-// they need only the other workgroups' phase A, not the routing. The wave
-// reads them once wave 0 has seen every logit (published after the shared
-// activations), rather than polling them while they are produced.
-template <int CPL_I, int SB, int KS, int NV>
-__device__ __forceinline__ void shared_down_early(const Args& a, const Ctx& c) {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's phase A reads of its ring are done
-  const uint32_t base = lds_addr(S.ring[c.wave]);
-  const int ns = n_s_tasks(a, c);
-  for (int i0 = 0; i0 < ns; i0 += 2) {
-    const int i1 = min(ns, i0 + 2);
-    for (int i = i0; i < i1; ++i) dma_task(s_task(a, c, i), base + (i - i0) * kHalf);
-    if (i0 == 0) {
-      wait_lds_epoch(&S.logit_ep, c.ep, a.status);
-      fetch_a<NV>(a, c, c.k);
-    }
-    wait_vm(0);
-    for (int i = i0; i < i1; ++i) {
-      const Task t = s_task(a, c, i);
-      MOE_T1_BITS(SB, c.sbits, B, down_rows<B, CPL_I, KS>(a, c, t, S.ring[c.wave] + (i - i0) * kHalf));
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // ring reads done before a refill
+// The shared expert's down rows of this workgroup's slice. Their weights and
+// inputs do not depend on the routing: the last wave streams the rows into
+// S.sd right after phase A and reads the shared activations (published in
+// phase A) once wave 0 has seen every logit (published after them), all
+// while wave 0 routes. The rows are computed, one task per wave, after each
+// wave has published its routed activations, while the waves wait for the
+// other workgroups' ready flags.
+template <int NV>
+__device__ __forceinline__ void shared_down_fetch(const Args& a, const Ctx& c) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const uint32_t base = lds_addr(S.sd);
+  const int tb = s_task(a, c, 0).bytes;
+  for (int i = 0; i < n_s_tasks(a, c); ++i) dma_task(s_task(a, c, i), base + i * tb);
+  wait_lds_epoch(&S.logit_ep, c.ep, a.status);
+  fetch_a<NV>(a, c, c.k);  // its waits also complete the weight loads above
+}
+template <int CPL_I, int SB, int KS>
+__device__ __forceinline__ void shared_down_part(const Args& a, const Ctx& c) {
+  const int tb = s_task(a, c, 0).bytes;
+  for (int i = c.wave; i < n_s_tasks(a, c); i += kWaves) {
+    const Task t = s_task(a, c, i);
+    MOE_T1_BITS(SB, c.sbits, B, down_rows<B, CPL_I, KS>(a, c, t, S.sd + i * tb));
   }
 }
 
@@ -868,6 +875,7 @@ __device__ __forceinline__ void phases_bc(const Args& a, const Ctx& c) {
     for (int j = j0; j < j1; ++j) {
       if (j == mb && !exchanged) {
         publish_a(a, c);
+        shared_down_part<CPL_I, SB, KS>(a, c);
         exchanged = true;
       }
       const Task t = task(j);
@@ -884,6 +892,7 @@ __device__ __forceinline__ void phases_bc(const Args& a, const Ctx& c) {
         });
         if (j + 1 == mb) {  // the wave's last routed pair: publish without waiting for the next batch
           publish_a(a, c);
+          shared_down_part<CPL_I, SB, KS>(a, c);
           exchanged = true;
         }
       } else {
@@ -895,7 +904,10 @@ __device__ __forceinline__ void phases_bc(const Args& a, const Ctx& c) {
     if (h) fill(1, bs1, be1, bn1);
     else fill(0, bs0, be0, bn0);
   }
-  if (!exchanged) publish_a(a, c);
+  if (!exchanged) {
+    publish_a(a, c);
+    shared_down_part<CPL_I, SB, KS>(a, c);
+  }
 }
 
 // ---- combine: h_{l+1}[j] = bf16(h_l[j] + sum_i w_i y_i[j] + sg y_s[j])
@@ -1049,7 +1061,7 @@ __global__ void __launch_bounds__(kThreads) stack1_kernel(Args a) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // routing stored before its flag
       *(volatile uint32_t*)&S.route_ep = c.ep;
     } else if (c.wave == kWaves - 1) {
-      shared_down_early<CPL_I, SB, SH::KS, SH::NV>(a, c);
+      shared_down_fetch<SH::NV>(a, c);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // phase A ring reads done
     wait_lds_epoch(&S.route_ep, c.ep, a.status);  // wave 0's routing is in LDS
@@ -1111,6 +1123,10 @@ int32_t launch_stack_t1(const moe_shape_t& s, const moe_layer_layout_t& L, const
     return MOE_ERR_UNSUPPORTED;
   const int a_tasks = (ra + rpw_h - 1) / rpw_h + (sa + rpw_h - 1) / rpw_h;
   if ((a_tasks + kWaves - 1) / kWaves * std::max(router_task, shared_task) > kRingBytes) return MOE_ERR_UNSUPPORTED;
+  // the shared expert's down rows of a slice fit S.sd
+  const int ds = s_task_rows(J, s.shared_inter);
+  if ((J + ds - 1) / ds * task_bytes(s.shared_bits, s.shared_inter, ds, false) > kRingBytes)
+    return MOE_ERR_UNSUPPORTED;
   const int pb = (s.top_k * s.inter + nwg - 1) / nwg;
   // a slot's activations: at most 32 per lane, from at most 128 workgroups
   if (imax > 32 * 64 || s.inter / pb + 2 > 128) return MOE_ERR_UNSUPPORTED;
