@@ -23,10 +23,10 @@
 // writer stores all of them and workgroup w reads copy w % n_copy, so that no
 // cache line is polled by every compute unit. The activations, which every
 // workgroup reads in full, are not polled while they are produced: each
-// workgroup sets a ready flag once it has stored its share, a consumer waits
-// for the flags of the workgroups that computed the slot it needs (one word
-// per workgroup) and then reads the activations once, still checking their
-// tags.
+// workgroup sets a ready flag once it has stored its share, a consumer reads
+// the slot it needs once, waits for the flags of the workgroups that computed
+// it (one word per workgroup) and then reads again only the words whose tags
+// were not yet current.
 //
 // Per layer and workgroup (8 waves, one workgroup per compute unit, as many
 // workgroups as the hidden state has slices of J rows):
