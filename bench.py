@@ -70,10 +70,12 @@ def kernel_path(w) -> str:
     """What one moe_decode_stack call launches for this workload."""
     if w.T == 1:
         return f"stack1_kernel: all {w.n_layers} layers in one launch (timed with its clear kernel)"
+    if w.T <= 3:
+        return f"stack_kernel: all {w.n_layers} layers in one launch (timed with its clear kernel)"
     if w.T > 8 and w.router_bits == 8 and w.shared_bits == 8:
-        return (f"per-layer kernels: route_mfma, down_mfma, expert, down per layer ({w.n_layers} layers, "
-                f"timed together)")
-    return f"stack_kernel: all {w.n_layers} layers in one launch (timed with its clear kernel)"
+        return (f"per-layer kernels: route_mfma, down_mfma, select, expert, down per layer ({w.n_layers} "
+                f"layers, timed together)")
+    return f"per-layer kernels: route, select, expert, down per layer ({w.n_layers} layers, timed together)"
 
 
 def copy_probe(mib: int) -> int:
@@ -166,6 +168,7 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
+    ap.add_argument("--rows", type=int, default=0, help="token rows per step (default: the workload's T)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding of this "
@@ -180,6 +183,10 @@ def main() -> int:
     from quantized_moe_decode_softmax_amd.runtime import DeviceStack
 
     w = WORKLOADS[args.workload]
+    if args.rows:
+        import dataclasses
+
+        w = dataclasses.replace(w, T=args.rows)
     T, L, K, W = w.T, w.n_layers, args.steps, args.warmup
     ds = DeviceStack.from_workload(w)
     xs = [ds.rows(1000 + s, T) for s in range(W + K)]
@@ -216,7 +223,7 @@ def main() -> int:
     tok_s = T * K / wall
     gbps = tb / (wall * 1e9)
     kernel_gbps = tb / K / launch_s / 1e9
-    tr = TRAFFIC.get(args.workload)
+    tr = TRAFFIC.get(args.workload) if T == WORKLOADS[args.workload].T else None
     traffic = traffic_detail = None
     if tr is not None and tr["src_hash"] == kernel_source_hash():
         traffic = tr["fetch_bytes"] + tr["write_bytes"]

@@ -702,9 +702,10 @@ extern "C" int32_t moe_decode_stack(const moe_shape_t* shape, const void* const*
     if (e != hipSuccess) return set_error(MOE_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
   }
   // One persistent kernel per up to 64 layers when the call allows it: the
-  // one-row streaming kernel, else the general one. MOE_STACK_KERNEL selects
-  // a path for comparison: 0 = per-layer kernels only, 1 = never the
-  // streaming kernel. All paths give the same results bit for bit.
+  // one-row streaming kernel, else the general one for few rows.
+  // MOE_STACK_KERNEL selects a path for comparison: 0 = per-layer kernels
+  // only, 1 = never the streaming kernel. All paths give the same results bit
+  // for bit.
   static const int stack_kernel_mode = [] {
     const char* v = getenv("MOE_STACK_KERNEL");
     return v && (v[0] == '0' || v[0] == '1') ? v[0] - '0' : 2;
@@ -715,8 +716,13 @@ extern "C" int32_t moe_decode_stack(const moe_shape_t* shape, const void* const*
     if (rc != MOE_ERR_UNSUPPORTED) return rc;
     clear_error();
   }
-  // calls on the matrix-core path (T > 8) run layer by layer
-  if (stack_kernel_mode >= 1 && !P.mfma) {
+  // The general persistent kernel is used for T <= 3 (measured on MI355X: up
+  // to 16% faster than the per-layer kernels at T = 2, slower from T = 4 on,
+  // where one workgroup routing all rows and wider expert tasks pay off);
+  // MOE_STACK_KERNEL=1 uses it for every T it handles. Calls on the
+  // matrix-core path (T > 8) always run layer by layer.
+  constexpr int kPersistMaxT = 3;
+  if (!P.mfma && (stack_kernel_mode == 1 || (stack_kernel_mode == 2 && T <= kPersistMaxT))) {
     rc = launch_stack_persistent(*shape, L, m, (uint8_t*)ws_dev, layers_host, n_layers, T, h_in_dev, h_out_dev,
                                  ids_dev, w_dev, h_trace_dev, st);
     if (rc != MOE_ERR_UNSUPPORTED) return rc;
