@@ -165,8 +165,10 @@ namespace moe {
 namespace {
 
 // ----------------------------------------------------------- route kernel
+// token rows t0, t0 + ts, ... of the call
 template <int BITS, int CPL>
-__device__ __forceinline__ void router_task(const Dims& d, const Ptrs& p, int task, int li, int lpr, int sr, int rpw) {
+__device__ __forceinline__ void router_task(const Dims& d, const Ptrs& p, int task, int li, int lpr, int sr, int rpw,
+                                            int t0, int ts) {
   constexpr int R = TaskRows<CPL>::R;
   int rows[R];
 #pragma unroll
@@ -183,7 +185,7 @@ __device__ __forceinline__ void router_task(const Dims& d, const Ptrs& p, int ta
     for (int r = 0; r < R; ++r) rp[r] = rows[r] >= 0 ? w + (int64_t)rows[r] * d.H : nullptr;
     RowsD<CPL, R> Q;
     load_dense_rows<CPL, R>(Q, rp, d.H, li, lpr);
-    for (int t = 0; t < d.T; ++t) {
+    for (int t = t0; t < d.T; t += ts) {
       prep_x<kDense, CPL>(x, p.h_in + (int64_t)t * d.H, d.H, li, lpr);
       if (task == 0) row_stats<kDense, CPL>(d, p, t, li, lpr, sr, x);
       dot_dense_rows<CPL, R>(Q, x, out);
@@ -207,7 +209,7 @@ __device__ __forceinline__ void router_task(const Dims& d, const Ptrs& p, int ta
     RowsQ<BITS, CPL, R> Q;
     load_rows<BITS, CPL, R>(Q, rc, rs, d.H, (int)(rb >> 2), li, lpr);
     XLane<BITS, CPL> x;
-    for (int t = 0; t < d.T; ++t) {
+    for (int t = t0; t < d.T; t += ts) {
       prep_x<BITS, CPL>(x, p.h_in + (int64_t)t * d.H, d.H, li, lpr);
       if (task == 0) row_stats<BITS, CPL>(d, p, t, li, lpr, sr, x);
       dot_rows<BITS, CPL, R, 1>(Q, x, x, out);
@@ -278,24 +280,27 @@ __device__ __forceinline__ void swiglu_task(const Dims& d, const Ptrs& p, const 
     default: { constexpr int B = 8; __VA_ARGS__; } break; \
   }
 
-// grid: n_router_tasks + n_shared_tasks workgroups of one wave.
+// grid: n_router_tasks + n_shared_tasks workgroups of min(T, 4) waves; each
+// wave loads the task's weight rows and takes token rows wave, wave + nw, ...
+// (a row's arithmetic does not depend on which wave computes it)
 template <int CPL>
-__global__ void __launch_bounds__(64, 2) route_kernel(Dims d, Ptrs p, int n_rt) {
-  const int lane = threadIdx.x, task = blockIdx.x;
+__global__ void __launch_bounds__(256) route_kernel(Dims d, Ptrs p, int n_rt) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6, task = blockIdx.x;
   const int lpr = lanes_per_row(d.H), rpw = 64 / lpr, sr = lane / lpr, li = lane % lpr;
   if (task < n_rt) {
     if (d.rbits == kDense) {
-      router_task<kDense, CPL>(d, p, task, li, lpr, sr, rpw);
+      router_task<kDense, CPL>(d, p, task, li, lpr, sr, rpw, wave, nw);
     } else {
-      MOE_BITS_CASES(d.rbits, B, router_task<B, CPL>(d, p, task, li, lpr, sr, rpw));
+      MOE_BITS_CASES(d.rbits, B, router_task<B, CPL>(d, p, task, li, lpr, sr, rpw, wave, nw));
     }
   } else {
     constexpr int RP = TaskRows<CPL>::R / 2;
     const int i0 = (task - n_rt) * RP * rpw;
-    const uint32_t all = d.T >= 32 ? 0xFFFFFFFFu : ((1u << d.T) - 1u);
+    uint32_t rows = 0u;
+    for (int t = wave; t < d.T; t += nw) rows |= 1u << t;
     MOE_BITS_CASES(d.sbits, B,
-                   swiglu_task<B, CPL, RP>(d, p, p.layer + d.off_shared, d.off_shared_up, d.Is, i0, all, d.k, -1, nullptr,
-                                       nullptr, li, lpr, sr, rpw));
+                   swiglu_task<B, CPL, RP>(d, p, p.layer + d.off_shared, d.off_shared_up, d.Is, i0, rows, d.k, -1,
+                                           nullptr, nullptr, li, lpr, sr, rpw));
   }
 }
 
@@ -559,7 +564,8 @@ LayerPlan make_plan(const moe_shape_t& s, const moe_layer_layout_t& L, int T) {
 
 template <int CPL>
 void launch_route(const LayerPlan& P, const Ptrs& p, hipStream_t st) {
-  route_kernel<CPL><<<P.n_rt + P.n_st, 64, 0, st>>>(P.d, p, P.n_rt);
+  const int nw = P.d.T < 4 ? P.d.T : 4;
+  route_kernel<CPL><<<P.n_rt + P.n_st, 64 * nw, 0, st>>>(P.d, p, P.n_rt);
 }
 template <int CPL>
 void launch_expert(const LayerPlan& P, const Ptrs& p, hipStream_t st) {
