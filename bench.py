@@ -70,7 +70,7 @@ def kernel_path(w) -> str:
     """What one moe_decode_stack call launches for this workload."""
     if w.T == 1:
         return f"stack1_kernel: all {w.n_layers} layers in one launch (timed with its clear kernel)"
-    if w.T <= 3:
+    if w.T <= 2:
         return f"stack_kernel: all {w.n_layers} layers in one launch (timed with its clear kernel)"
     if w.T > 8 and w.router_bits == 8 and w.shared_bits == 8:
         return (f"per-layer kernels: route_mfma, down_mfma, select, expert, down per layer ({w.n_layers} "

@@ -722,12 +722,12 @@ extern "C" int32_t moe_decode_stack(const moe_shape_t* shape, const void* const*
     if (rc != MOE_ERR_UNSUPPORTED) return rc;
     clear_error();
   }
-  // The general persistent kernel is used for T <= 3 (measured on MI355X: up
-  // to 16% faster than the per-layer kernels at T = 2, slower from T = 4 on,
-  // where one workgroup routing all rows and wider expert tasks pay off);
-  // MOE_STACK_KERNEL=1 uses it for every T it handles. Calls on the
-  // matrix-core path (T > 8) always run layer by layer.
-  constexpr int kPersistMaxT = 3;
+  // The general persistent kernel is used for T <= 2 (measured on MI355X:
+  // 11% faster than the per-layer kernels at T = 2, slower from T = 3 on,
+  // where routing once per call, wider expert tasks and token rows spread
+  // over waves pay off); MOE_STACK_KERNEL=1 uses it for every T it handles.
+  // Calls on the matrix-core path (T > 8) always run layer by layer.
+  constexpr int kPersistMaxT = 2;
   if (!P.mfma && (stack_kernel_mode == 1 || (stack_kernel_mode == 2 && T <= kPersistMaxT))) {
     rc = launch_stack_persistent(*shape, L, m, (uint8_t*)ws_dev, layers_host, n_layers, T, h_in_dev, h_out_dev,
                                  ids_dev, w_dev, h_trace_dev, st);

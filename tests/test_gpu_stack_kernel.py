@@ -55,7 +55,7 @@ VARIANTS = [
 
 
 @pytest.mark.parametrize("name,kw", VARIANTS, ids=[v[0] for v in VARIANTS])
-@pytest.mark.parametrize("T", [1, 3])
+@pytest.mark.parametrize("T", [1, 2])
 def test_stack_kernel_variant(name, kw, T):
     n_layers = 3
     ds = DeviceStack(kw, n_layers, t_max=32, seed=11)
