@@ -419,7 +419,7 @@ __device__ __forceinline__ void down_unit(const Dims& d, const Ptrs& p, const ui
 }
 
 template <int CPL, int RD>
-__global__ void __launch_bounds__(1024) down_kernel(Dims d, Ptrs p, int J) {
+__device__ __forceinline__ void down_body(const Dims& d, const Ptrs& p, int J) {
   __shared__ float s_D[kMaxT * (kMaxTopK + 1) * 16];
   __shared__ int s_ids[kMaxT * kMaxTopK];
   __shared__ float s_w[kMaxT * kMaxTopK];
@@ -472,6 +472,19 @@ __global__ void __launch_bounds__(1024) down_kernel(Dims d, Ptrs p, int J) {
   }
 }
 
+// up to 16 waves (one per unit in flight), RD * CPL <= 4
+template <int CPL, int RD>
+__global__ void __launch_bounds__(1024) down_kernel(Dims d, Ptrs p, int J) {
+  down_body<CPL, RD>(d, p, J);
+}
+// up to 8 waves with 8 rows per lane group (J = 16 at K <= 1024): for many
+// token rows, where each unit's activations are read once per workgroup and
+// a wider slice halves those reads
+template <int CPL, int RD>
+__global__ void __launch_bounds__(512) down_kernel_wide(Dims d, Ptrs p, int J) {
+  down_body<CPL, RD>(d, p, J);
+}
+
 // Status word of a stack call that runs layer by layer: no wait can time out.
 __global__ void clear_status_kernel(uint32_t* status) { status[threadIdx.x] = 0u; }
 
@@ -481,6 +494,7 @@ struct LayerPlan {
   int cpl_h, cpl_i;
   int n_rt, n_st, tpu, g_grid;
   int J, RD, d_grid, d_threads;
+  bool d_wide;
   // matrix-core router and shared expert (T > 8, 8-bit router and shared)
   bool mfma;
   int m_nt, m_ng_route, m_ng_down, m_rt, m_pt, m_down;
@@ -536,18 +550,26 @@ LayerPlan make_plan(const moe_shape_t& s, const moe_layer_layout_t& L, int T) {
   P.g_grid = (waves + 3) / 4;
   if (P.g_grid > 2048) P.g_grid = 2048;
   // down: J output rows per workgroup (about 256 workgroups), RD rows per lane
-  // group for the longest K, with RD * chunks <= 4 to bound registers
+  // group for the longest K, with RD * chunks <= 4 to bound registers; from
+  // 16 token rows on, one chunk per lane, a wide variant with RD = 8 and at
+  // most 8 waves (J up to 16)
   const int rpw_min = 64 / lanes_per_row(d.imax);  // rows per pass of the longest K
-  const int rd_max = 4 / P.cpl_i;
+  P.d_wide = T >= 16 && P.cpl_i == 1;
+  const int rd_max = P.d_wide ? 8 : 4 / P.cpl_i;
   int J = pow2ceil((s.hidden + 255) / 256);
   if (J < rpw_min) J = rpw_min;
   if (J > rpw_min * rd_max) J = rpw_min * rd_max;
   if (J > 16) J = 16;
   P.J = J;
   P.RD = (J + rpw_min - 1) / rpw_min;
+  if (P.d_wide && P.RD != 8) P.d_wide = false;  // the wide variant is compiled for RD = 8 only
+  if (!P.d_wide && P.RD * P.cpl_i > 4) {  // back to the narrow bound
+    P.J = J = rpw_min * (4 / P.cpl_i);
+    P.RD = 4 / P.cpl_i;
+  }
   P.d_grid = (s.hidden + P.J - 1) / P.J;
   int nw = max_units + 1;
-  if (nw > 16) nw = 16;
+  if (nw > (P.d_wide ? 8 : 16)) nw = P.d_wide ? 8 : 16;
   P.d_threads = 64 * nw;
   P.mfma = T >= kMfmaMinT && s.router_bits == 8 && s.shared_bits == 8 && mfma_enabled();
   P.m_nt = T > 16 ? 2 : 1;
@@ -627,8 +649,10 @@ int32_t launch_layer(const LayerPlan& P, const WsMap& m, uint8_t* ws, const uint
     MOE_CPL_CASES(P.cpl_h, C, launch_route<C>(P, p, st));
   }
   MOE_CPL_CASES(P.cpl_h, C, launch_expert<C>(P, p, st));
-  // rows x chunks per lane <= 4 (make_plan)
-  switch (P.cpl_i * 8 + P.RD) {
+  // rows x chunks per lane <= 4 (make_plan), or the wide variant
+  if (P.d_wide) {
+    down_kernel_wide<1, 8><<<P.d_grid, P.d_threads, 0, st>>>(P.d, p, P.J);
+  } else switch (P.cpl_i * 8 + P.RD) {
     case 8 + 1: launch_down<1, 1>(P, p, st); break;
     case 8 + 2: launch_down<1, 2>(P, p, st); break;
     case 8 + 4: launch_down<1, 4>(P, p, st); break;
