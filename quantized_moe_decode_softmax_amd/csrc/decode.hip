@@ -304,6 +304,58 @@ __global__ void __launch_bounds__(256) route_kernel(Dims d, Ptrs p, int n_rt) {
   }
 }
 
+// Routed experts for many token rows, one token row at a time per wave:
+// tasks are ordered (row t, slot, block of row pairs), a wave takes a run of
+// them, arranges x_t once per row and streams the gate/up rows of the row's
+// experts (an expert used by several rows is read once per row). The
+// arithmetic of a (row, pair) is the one of swiglu_task.
+template <int BITS, int CPL, int RP>
+__device__ __forceinline__ void swiglu_rows(const Dims& d, const Ptrs& p, int task0, int task1, int tps, int li,
+                                            int lpr, int sr, int rpw) {
+  constexpr int R = 2 * RP;
+  const int64_t rb = row_bytes(BITS, d.H);
+  const int64_t cb = matrix_codes_bytes(BITS, d.I, d.H);
+  const int per_row = d.k * tps;
+  XLane<BITS, CPL> x;
+  int cur_t = -1;
+  float r = 0.f;
+  for (int task = task0; task < task1; ++task) {
+    const int t = task / per_row, rem = task % per_row, slot = rem / tps, i0 = (rem % tps) * RP * rpw;
+    if (t != cur_t) {  // wave-uniform
+      prep_x<BITS, CPL>(x, p.h_in + (int64_t)t * d.H, d.H, li, lpr);
+      r = p.rinv[t];
+      cur_t = t;
+    }
+    const int e = p.ids[t * d.k + slot];
+    const uint8_t* gate = p.layer + d.off_e0 + (int64_t)e * d.e_stride;
+    const uint8_t* up = gate + d.off_e_up;
+    const uint32_t* gsb = (const uint32_t*)(gate + cb);
+    const uint32_t* usb = (const uint32_t*)(up + cb);
+    int pairs[RP];
+    const uint8_t* rc[R];
+    const uint32_t* rs[R];
+#pragma unroll
+    for (int q = 0; q < RP; ++q) {
+      const int i = i0 + sr + rpw * q;
+      pairs[q] = i < d.I ? i : -1;
+      rc[q] = i < d.I ? gate + (int64_t)i * rb : nullptr;
+      rs[q] = i < d.I ? gsb + (int64_t)i * (d.H >> 6) : nullptr;
+      rc[RP + q] = i < d.I ? up + (int64_t)i * rb : nullptr;
+      rs[RP + q] = i < d.I ? usb + (int64_t)i * (d.H >> 6) : nullptr;
+    }
+    RowsQ<BITS, CPL, R> Q;
+    load_rows<BITS, CPL, R>(Q, rc, rs, d.H, (int)(rb >> 2), li, lpr);
+    float out[R];
+    dot_rows<BITS, CPL, R, 1>(Q, x, x, out);
+#pragma unroll
+    for (int q = 0; q < RP; ++q) {
+      const float g = reduce_row(out[q], lpr) * r;
+      const float v = reduce_row(out[RP + q], lpr) * r;
+      if (pairs[q] >= 0 && li == lpr - 1) store_a(d, p, t, slot, pairs[q], silu_mul(g, v));
+    }
+  }
+}
+
 // ---------------------------------------------------------- select kernel
 // Routing of the call, once: top-k of every token row (row t on wave t % 16),
 // the renormalised weights, and the ascending list of experts used by any
@@ -376,6 +428,18 @@ __global__ void __launch_bounds__(256, 2) expert_kernel(Dims d, Ptrs p, int task
                    swiglu_task<B, CPL, RP>(d, p, blk, d.off_e_up, d.I, i0, s_masks[u], -1, e, s_ids, s_r, li, lpr, sr,
                                        rpw));
   }
+}
+
+// grid: waves of tpw consecutive (row, slot, block) tasks, tps blocks per slot
+template <int CPL>
+__global__ void __launch_bounds__(256, 2) expert_rows_kernel(Dims d, Ptrs p, int tps, int tpw) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lpr = lanes_per_row(d.H), rpw = 64 / lpr, sr = lane / lpr, li = lane % lpr;
+  constexpr int RP = ExpertPairs<CPL>::RP;
+  const int n_tasks = d.T * d.k * tps;
+  const int task0 = (blockIdx.x * 4 + wave) * tpw;
+  const int task1 = task0 + tpw < n_tasks ? task0 + tpw : n_tasks;
+  MOE_BITS_CASES(d.ebits, B, swiglu_rows<B, CPL, RP>(d, p, task0, task1, tps, li, lpr, sr, rpw));
 }
 
 // ------------------------------------------------------------ down kernel
@@ -489,10 +553,14 @@ __global__ void __launch_bounds__(512) down_kernel_wide(Dims d, Ptrs p, int J) {
 __global__ void clear_status_kernel(uint32_t* status) { status[threadIdx.x] = 0u; }
 
 // ---------------------------------------------------------------- launch
+// from this many token rows the routed experts run row by row (expert_rows_kernel)
+constexpr int kRowsMinT = 16;
+
 struct LayerPlan {
   Dims d;
   int cpl_h, cpl_i;
   int n_rt, n_st, tpu, g_grid;
+  int rows_tpw, rows_grid;  // expert_rows_kernel (rows_grid > 0: used)
   int J, RD, d_grid, d_threads;
   bool d_wide;
   // matrix-core router and shared expert (T > 8, 8-bit router and shared)
@@ -549,6 +617,13 @@ LayerPlan make_plan(const moe_shape_t& s, const moe_layer_layout_t& L, int T) {
   const int waves = max_units * P.tpu;
   P.g_grid = (waves + 3) / 4;
   if (P.g_grid > 2048) P.g_grid = 2048;
+  // many token rows: one token row at a time per wave (about 8192 waves)
+  P.rows_grid = 0;
+  if (T >= kRowsMinT) {
+    const int n_tasks = T * d.k * P.tpu;
+    P.rows_tpw = (n_tasks + 8191) / 8192;
+    P.rows_grid = (n_tasks + 4 * P.rows_tpw - 1) / (4 * P.rows_tpw);
+  }
   // down: J output rows per workgroup (about 256 workgroups), RD rows per lane
   // group for the longest K, with RD * chunks <= 4 to bound registers; from
   // 16 token rows on, one chunk per lane, a wide variant with RD = 8 and at
@@ -592,7 +667,10 @@ void launch_route(const LayerPlan& P, const Ptrs& p, hipStream_t st) {
 template <int CPL>
 void launch_expert(const LayerPlan& P, const Ptrs& p, hipStream_t st) {
   select_kernel<<<1, 1024, 0, st>>>(P.d, p);
-  expert_kernel<CPL><<<P.g_grid, 256, 0, st>>>(P.d, p, P.tpu);
+  if (P.rows_grid > 0)
+    expert_rows_kernel<CPL><<<P.rows_grid, 256, 0, st>>>(P.d, p, P.tpu, P.rows_tpw);
+  else
+    expert_kernel<CPL><<<P.g_grid, 256, 0, st>>>(P.d, p, P.tpu);
 }
 template <int NT>
 void launch_mfma(const LayerPlan& P, const Ptrs& p, hipStream_t st) {
