@@ -47,7 +47,7 @@ KERNEL_SOURCES = ["stack1.hip", "gemv.h", "device_common.h"]  # the stack kernel
 # 256 MiB device copy measured the same way. Keyed by workload; valid only
 # for the kernel sources whose hash is stored with it.
 TRAFFIC = {
-    "a3b": {"src_hash": "8c844e517a323262", "fetch_bytes": 993_864_305, "write_bytes": 55_063_702},
+    "a3b": {"src_hash": "1b0eea5d7693d2c2", "fetch_bytes": 993_746_459, "write_bytes": 55_063_826},
 }
 
 
@@ -70,8 +70,6 @@ def kernel_path(w) -> str:
     """What one moe_decode_stack call launches for this workload."""
     if w.T == 1:
         return f"stack1_kernel: all {w.n_layers} layers in one launch (timed with its clear kernel)"
-    if w.T <= 2:
-        return f"stack_kernel: all {w.n_layers} layers in one launch (timed with its clear kernel)"
     if w.T > 8 and w.router_bits == 8 and w.shared_bits == 8:
         return (f"per-layer kernels: route_mfma, down_mfma, select, expert, down per layer ({w.n_layers} "
                 f"layers, timed together)")

@@ -179,7 +179,7 @@ int32_t moe_decode_layer(const moe_shape_t* shape, const void* layer_dev, int32_
 /*
  * A stack of n_layers MoE layers with distinct weights: h_0 = h_in,
  * h_{l+1} = bf16(layer_l(h_l)), h_out = h_{n_layers}. The host never waits
- * inside the stack. For T <= 2 each group of up to 64 layers runs as one
+ * inside the stack. For T = 1 each group of up to 64 layers runs as one
  * kernel with one workgroup per compute unit whose workgroups wait on each
  * other's results (bounded waits; see moe_stack_status); other calls run as
  * kernels per layer (the same as moe_decode_layer). Both give the same

@@ -24,8 +24,7 @@ LIB = os.path.join(PKG, "libmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["gen.hip", "decode.hip", "persist.hip", "persist_11.hip", "persist_12.hip", "persist_21.hip",
-               "stack1.hip"]
+HIP_SOURCES = ["gen.hip", "decode.hip", "stack1.hip"]
 HOST_SOURCES = ["moe_host.cpp"]
 HIP_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -554,7 +554,7 @@ __global__ void clear_status_kernel(uint32_t* status) { status[threadIdx.x] = 0u
 
 // ---------------------------------------------------------------- launch
 // from this many token rows the routed experts run row by row (expert_rows_kernel)
-constexpr int kRowsMinT = 16;
+constexpr int kRowsMinT = 2;
 
 struct LayerPlan {
   Dims d;
@@ -809,30 +809,20 @@ extern "C" int32_t moe_decode_stack(const moe_shape_t* shape, const void* const*
     hipError_t e = hipMemcpyAsync(h_trace_dev, h_in_dev, th * 2, hipMemcpyDeviceToDevice, st);
     if (e != hipSuccess) return set_error(MOE_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
   }
-  // One persistent kernel per up to 64 layers when the call allows it: the
-  // one-row streaming kernel, else the general one for few rows.
-  // MOE_STACK_KERNEL selects a path for comparison: 0 = per-layer kernels
-  // only, 1 = never the streaming kernel. All paths give the same results bit
-  // for bit.
-  static const int stack_kernel_mode = [] {
+  // One-row calls run as one streaming kernel per up to 64 layers when the
+  // shape allows it; every other call runs layer by layer (measured on
+  // MI355X, the per-layer kernels now beat a persistent kernel for T >= 2:
+  // one select kernel routes all rows, the routed experts go row by row, the
+  // route kernel spreads token rows over waves). MOE_STACK_KERNEL=0 runs
+  // one-row calls layer by layer too, for comparison; both give the same
+  // results bit for bit.
+  static const bool streaming = [] {
     const char* v = getenv("MOE_STACK_KERNEL");
-    return v && (v[0] == '0' || v[0] == '1') ? v[0] - '0' : 2;
+    return !(v && v[0] == '0');
   }();
-  if (stack_kernel_mode == 2) {
+  if (streaming) {
     rc = launch_stack_t1(*shape, L, m, (uint8_t*)ws_dev, layers_host, n_layers, T, h_in_dev, h_out_dev, ids_dev,
                          w_dev, h_trace_dev, st);
-    if (rc != MOE_ERR_UNSUPPORTED) return rc;
-    clear_error();
-  }
-  // The general persistent kernel is used for T <= 2 (measured on MI355X:
-  // 11% faster than the per-layer kernels at T = 2, slower from T = 3 on,
-  // where routing once per call, wider expert tasks and token rows spread
-  // over waves pay off); MOE_STACK_KERNEL=1 uses it for every T it handles.
-  // Calls on the matrix-core path (T > 8) always run layer by layer.
-  constexpr int kPersistMaxT = 2;
-  if (!P.mfma && (stack_kernel_mode == 1 || (stack_kernel_mode == 2 && T <= kPersistMaxT))) {
-    rc = launch_stack_persistent(*shape, L, m, (uint8_t*)ws_dev, layers_host, n_layers, T, h_in_dev, h_out_dev,
-                                 ids_dev, w_dev, h_trace_dev, st);
     if (rc != MOE_ERR_UNSUPPORTED) return rc;
     clear_error();
   }

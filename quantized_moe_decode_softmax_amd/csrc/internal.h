@@ -56,14 +56,9 @@ struct WsMap {
   int64_t a_lo;         // bf16  [T][k+1][Imax]  low part: a = hi + lo to 16 significant bits
   int64_t hbuf;         // bf16  [2][T][H] ping-pong for stacks
   int64_t ysh;          // float [T][H]  shared expert's down projection (matrix-core path)
-  // stack kernel exchange buffers: 64-bit words = 32-bit payload | epoch << 32
-  int64_t tg_h;         // u64 [T][H/2]       hidden state, two bf16 per word
-  int64_t tg_logit;     // u64 [T][E]         raw router dot products
-  int64_t tg_rs;        // u64 [T][2]         RMS factor, shared-expert gate
-  int64_t tg_a;         // u64 [T][k+1][Imax] activations, bf16 hi | bf16 lo << 16
-  // one-row streaming stack kernel (stack1.hip): the same word format, each
-  // buffer in n_copy copies (stride *_cs words) that writers all store and
-  // workgroup w reads copy w % n_copy; sized for one token row
+  // one-row streaming stack kernel (stack1.hip): exchange buffers of 64-bit
+  // words = 32-bit payload | epoch << 32, each in n_copy copies (stride *_cs
+  // words) that writers all store and workgroup w reads copy w % n_copy
   int n_copy;
   int64_t x_h;          // u64 [2][n_copy][H/2]      hidden state by layer parity
   int64_t x_logit;      // u64 [n_copy][E]           raw router dot products
@@ -71,7 +66,7 @@ struct WsMap {
   int64_t x_flag;       // u64 [n_copy][512]         per workgroup: its activations are stored
   int64_t xh_cs, xl_cs, xa_cs;
   int64_t status;       // u32 [64]           word 0: nonzero after a timed-out wait
-  int64_t tg_end;       // end of the region the stack kernel clears per call
+  int64_t x_end;        // end of the region the streaming kernel clears per call
   int64_t total;
 };
 
@@ -83,12 +78,6 @@ void clear_error();
 
 int32_t check_shape(const moe_shape_t* s);
 
-// Stack decode with the persistent kernel (persist.hip). MOE_ERR_UNSUPPORTED,
-// with nothing launched, for shapes it does not handle.
-struct WsMap;
-int32_t launch_stack_persistent(const moe_shape_t& s, const moe_layer_layout_t& L, const WsMap& m, uint8_t* ws,
-                                const void* const* layers, int n_layers, int T, const uint16_t* h_in, uint16_t* h_out,
-                                int32_t* ids_out, float* w_out, uint16_t* h_trace_out, moe_stream_t st);
 void layout_of(const moe_shape_t& s, moe_layer_layout_t* out);
 
 // One-row stack decode with the streaming kernel (stack1.hip).

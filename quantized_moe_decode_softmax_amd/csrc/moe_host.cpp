@@ -86,10 +86,6 @@ WsMap ws_map(const moe_shape_t& s, int T) {
   m.a_lo = take((int64_t)T * (k + 1) * imax * 2);
   m.hbuf = take((int64_t)2 * T * s.hidden * 2);
   m.ysh = take((int64_t)T * s.hidden * 4);
-  m.tg_h = take((int64_t)T * (s.hidden / 2) * 8);
-  m.tg_logit = take((int64_t)T * s.n_experts * 8);
-  m.tg_rs = take((int64_t)T * 2 * 8);
-  m.tg_a = take((int64_t)T * (k + 1) * imax * 8);
   m.n_copy = kExchangeCopies;
   m.xh_cs = align_up(s.hidden / 2, 512);
   m.xl_cs = align_up(s.n_experts, 512);
@@ -99,7 +95,7 @@ WsMap ws_map(const moe_shape_t& s, int T) {
   m.x_a = take(m.n_copy * m.xa_cs * 8);
   m.x_flag = take(m.n_copy * 512 * 8);
   m.status = take(64 * 4);
-  m.tg_end = off;
+  m.x_end = off;
   m.total = off;
   return m;
 }

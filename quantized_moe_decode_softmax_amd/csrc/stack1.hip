@@ -1214,7 +1214,7 @@ int32_t launch_stack_t1(const moe_shape_t& s, const moe_layer_layout_t& L, const
     a.w_out = w_out ? w_out + (int64_t)l0 * k : nullptr;
     a.h_trace = h_trace_out ? h_trace_out + (int64_t)(l0 + 1) * H : nullptr;
     // zero the exchange words and the status word (no stale epoch can match)
-    const int64_t nclr = (m.tg_end - m.x_h) / 8;
+    const int64_t nclr = (m.x_end - m.x_h) / 8;
     clear_words<<<64, 256, 0, st>>>((uint64_t*)(ws + m.x_h), nclr);
     launch(a, st);
     const hipError_t e = hipGetLastError();

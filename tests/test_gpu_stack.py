@@ -96,8 +96,9 @@ def test_a3b_stack_40_layers_T1(a3b):
 
 @pytest.mark.parametrize("T", [1, 2, 7])
 def test_a3b_stack_equals_layer_calls_and_is_deterministic(a3b, T):
-    """The stack call (one persistent kernel) and 40 chained one-layer calls
-    (three kernels each) compute every value in the same order: bitwise equal."""
+    """The stack call (one streaming kernel at T = 1, kernels per layer
+    otherwise) and 40 chained one-layer calls compute every value in the same
+    order: bitwise equal."""
     x = a3b.rows(1001 + T, T)
     out, ids, w, tr = a3b.stack(x, trace=True)
     out2, ids2, w2, _ = a3b.stack(x)

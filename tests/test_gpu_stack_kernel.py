@@ -1,13 +1,15 @@
-"""GPU tests of the persistent stack kernel over its compiled variants.
+"""GPU tests of moe_decode_stack over the compiled variants of its kernels.
 
-moe_decode_stack runs groups of up to 64 layers as one kernel (one workgroup
-per compute unit, cross-workgroup data exchange by polling). Its variants are
-chosen by the chunks per lane of the hidden and intermediate sizes and by the
-down-projection rows per lane group. One synthetic shape per variant (with
-ragged sizes, every code width and the dense router among them):
+One-row stacks run as one streaming kernel per up to 64 layers (one
+workgroup per compute unit, cross-workgroup data exchange by polling), with
+fixed-shape and generic instantiations; stacks of more rows run layer by
+layer, whose variants are chosen by the chunks per lane of the hidden and
+intermediate sizes and by the down-projection rows per lane group. One
+synthetic shape per variant (with ragged sizes, every code width and the
+dense router among them), at T = 1 and T = 2:
 
-* the stack equals chained one-layer calls (three kernels per layer) bit for
-  bit, outputs, ids and weights;
+* the stack equals chained one-layer calls bit for bit, outputs, ids and
+  weights;
 * the status word reports that every wait was met;
 * layer 0 of the stack agrees with the oracle (same input, pass criteria of
   tests/parity.py);
