@@ -1,24 +1,28 @@
 // MoE decode kernels for gfx950 and the moe_decode_layer / moe_decode_stack
 // entry points.
 //
-// One layer is three stream-ordered kernels; each kernel boundary is one of
-// the layer's unavoidable all-to-all dependencies:
-//   route_kernel  (1 wave per workgroup) router dot products W_r h_t for every
-//                 token row t and expert, and, independent of routing, the
-//                 shared expert's SwiGLU activations; workgroup 0 also writes
-//                 the RMS factor r_t = 1/sqrt(mean(h_t^2) + eps) and the shared
-//                 expert's gate sigmoid(r_t gvec . h_t).
-//   expert_kernel every workgroup recomputes the routing (top-k of r_t W_r h_t,
-//                 ties to the lower id, softmax renormalised over the k) and
-//                 the sorted list of experts used by any row; its waves then
-//                 compute the SwiGLU activations silu(r W_g h) * (r W_u h) of
-//                 those experts, each expert's rows read once for all the
-//                 token rows that selected it.
+// One layer is four stream-ordered kernels; each boundary is one of the
+// layer's all-to-all dependencies:
+//   route_kernel  router dot products W_r h_t for every token row t and
+//                 expert, and, independent of routing, the shared expert's
+//                 SwiGLU activations (min(T, 4) waves per workgroup share the
+//                 token rows); workgroup 0 also writes the RMS factor
+//                 r_t = 1/sqrt(mean(h_t^2) + eps) and the shared expert's gate
+//                 sigmoid(r_t gvec . h_t). For T > 8 with an 8-bit router and
+//                 shared expert, route_mfma_kernel (mfma.h) does this on the
+//                 matrix cores and down_mfma_kernel the shared down projection.
+//   select_kernel one workgroup: top-k of r_t W_r h_t for every row (ties to
+//                 the lower id, softmax renormalised over the k) and the
+//                 ascending list of experts used by any row, with row masks.
+//   expert_kernel SwiGLU activations silu(r W_g h) * (r W_u h) of the selected
+//                 experts: at T = 1 by expert (each expert's rows read once for
+//                 all rows using it); from T = 2 expert_rows_kernel goes one
+//                 token row at a time per wave (the row's input arranged once).
 //   down_kernel   each workgroup owns a slice of output rows; one wave per
 //                 expert (routed and shared) computes W_d a for the rows that
 //                 use it; the slice is then combined in rank order:
 //                 h + sum_i w_i y_i + gate * y_shared, rounded to bf16
-//                 (nearest even).
+//                 (nearest even). down_kernel_wide: 16-row slices for T >= 16.
 // RMSNorm has weight 1, so W (r h) = r (W h): h is used as stored (bf16) and
 // r multiplies each dot product. The activations a are kept as two bf16 parts
 // a = hi + lo (16 significant bits) so the down projections also run on
@@ -31,9 +35,10 @@
 // normalisation, combine + residual + gate) and "Deferred GPU Expert Compute"
 // (combine and residual on the GPU, handed to the next layer directly).
 //
-// Determinism and row-exactness: no atomics touch data, every reduction has a
-// fixed order, and the arithmetic of one (token row, output) pair is the same
-// whatever T is and whichever rows share an expert.
+// Determinism and row-exactness: no atomics touch data (the select kernel's
+// LDS bit-OR of row masks does not depend on order), every reduction has a
+// fixed order, and on the vector-unit path the arithmetic of one (token row,
+// output) pair is the same whatever T is and whichever rows share an expert.
 #include <cmath>
 #include <cstdlib>
 
