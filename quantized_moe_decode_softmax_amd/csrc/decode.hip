@@ -95,21 +95,24 @@ __device__ __forceinline__ void prep_split(XLane<BITS, CPL>& xh, XLane<BITS, CPL
 #pragma unroll
   for (int m = 0; m < CPL; ++m) {
     const int c = li + lpr * m;
-    uint32_t w[32];
-    if (c < nch) {
-      uint32_t nh[16], nl[16];
-      load64B(hi + 32 * c, nh);
-      load64B(lo + 32 * c, nl);
+    // every lane loads (lanes past the row read its last chunk, then zero it,
+    // which is needed only when the row ends inside this pass)
+    const bool ok = c < nch;
+    const int cc = ok ? c : nch - 1;
+    uint32_t nh[16], nl[16];
+    load64B(hi + 32 * cc, nh);
+    load64B(lo + 32 * cc, nl);
+    if (lpr * (m + 1) > nch) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        w[2 * i] = __builtin_amdgcn_perm(nl[i], nh[i], 0x05040100u);
-        w[2 * i + 1] = __builtin_amdgcn_perm(nl[i], nh[i], 0x07060302u);
+        nh[i] = ok ? nh[i] : 0u;
+        nl[i] = ok ? nl[i] : 0u;
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) w[i] = 0u;
     }
-    split_arrange<BITS>(w, c, xh.w[m], xl.w[m]);
+    // the halves arranged separately: the same words as splitting the
+    // stack kernel's (hi | lo << 16) words after arranging them
+    arrange_chunk<BITS>(nh, c, xh.w[m]);
+    arrange_chunk<BITS>(nl, c, xl.w[m]);
     xh.s[m] = sum_words<XWords<BITS>::N>(xh.w[m]);
     xl.s[m] = sum_words<XWords<BITS>::N>(xl.w[m]);
   }
@@ -470,12 +473,14 @@ __device__ __forceinline__ void down_unit(const Dims& d, const Ptrs& p, const ui
   load_rows<BITS, CPL, RD>(Q, rc, rs, K, (int)(rb >> 2), li, lpr);
   XLane<BITS, CPL> xh, xl;
   float out[RD];
+  rowmask = __builtin_amdgcn_readfirstlane(rowmask);  // wave-uniform (read from LDS)
   for (int t = 0; t < d.T; ++t) {
     if (!(rowmask >> t & 1u)) continue;
     int slot = slot_fixed;
     if (slot < 0)
       for (int i = 0; i < d.k; ++i)
         if (s_ids[t * d.k + i] == e) slot = i;
+    slot = __builtin_amdgcn_readfirstlane(slot);
     const int64_t aoff = ((int64_t)t * (d.k + 1) + slot) * d.imax;
     prep_split<BITS, CPL>(xh, xl, p.a_hi + aoff, p.a_lo + aoff, K, li, lpr);
     dot_rows<BITS, CPL, RD, 2>(Q, xh, xl, out);
@@ -515,7 +520,7 @@ __device__ __forceinline__ void down_body(const Dims& d, const Ptrs& p, int J) {
   const uint32_t all = d.T >= 32 ? 0xFFFFFFFFu : ((1u << d.T) - 1u);
   for (int u = wave; u <= n_units; u += nw) {
     if (u < n_units) {
-      const int e = s_units[u];
+      const int e = __builtin_amdgcn_readfirstlane(s_units[u]);
       const uint8_t* mat = p.layer + d.off_e0 + (int64_t)e * d.e_stride + d.off_e_down;
       MOE_BITS_CASES(d.ebits, B, down_unit<B, CPL, RD>(d, p, mat, d.I, j0, J, s_masks[u], -1, e, s_ids, s_D));
     } else if (!p.ysh) {

@@ -249,12 +249,14 @@ __device__ __forceinline__ void prep_x(XLane<BITS, CPL>& x, const uint16_t* v, i
 #pragma unroll
   for (int m = 0; m < CPL; ++m) {
     const int c = li + lpr * m;
+    // every lane loads (lanes past the row read its last chunk, then zero it,
+    // which is needed only when the row ends inside this pass)
+    const bool ok = c < nch;
     uint32_t n[16];
-    if (c < nch) {
-      load64B(v + 32 * c, n);
-    } else {
+    load64B(v + 32 * (ok ? c : nch - 1), n);
+    if (lpr * (m + 1) > nch) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) n[i] = 0u;
+      for (int i = 0; i < 16; ++i) n[i] = ok ? n[i] : 0u;
     }
     if constexpr (BITS == 3) {
       switch ((2 * c) % 10) {
@@ -305,32 +307,39 @@ __device__ __forceinline__ float sumsq(const XLane<BITS, CPL>& x) {
 }
 
 // ------------------------------------------------------------ code loading
-// Raw packed words of chunk c (codes 32c .. 32c+31) of one row; up to 8 words.
+// Load of a T at p in global memory. The address space is explicit so that the
+// load is a global_load (tracked by vmcnt alone): a flat load also counts
+// against lgkmcnt, so every later LDS wait would wait for the weights too.
+template <class T>
+__device__ __forceinline__ T gload(const uint8_t* p) {
+  return *(const __attribute__((address_space(1))) T*)p;
+}
+
+// Raw packed words of chunk c (codes 32c .. 32c+31) of one row in global
+// memory; up to 8 words.
 template <int BITS>
 __device__ __forceinline__ void load_chunk(const uint8_t* row, int c, int row_words, uint32_t (&q)[8]) {
   if constexpr (BITS == 2) {
-    const u32x2 v = *(const u32x2*)(row + 8 * c);
+    const u32x2 v = gload<u32x2>(row + 8 * c);
     q[0] = v.x;
     q[1] = v.y;
   } else if constexpr (BITS == 4) {
-    const u32x4 v = *(const u32x4*)(row + 16 * c);
+    const u32x4 v = gload<u32x4>(row + 16 * c);
     q[0] = v.x;
     q[1] = v.y;
     q[2] = v.z;
     q[3] = v.w;
   } else if constexpr (BITS == 6) {
-    const u32x2* p = (const u32x2*)(row + 24 * c);
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
-      const u32x2 v = p[i];
+      const u32x2 v = gload<u32x2>(row + 24 * c + 8 * i);
       q[2 * i] = v.x;
       q[2 * i + 1] = v.y;
     }
   } else if constexpr (BITS == 8) {
-    const u32x4* p = (const u32x4*)(row + 32 * c);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const u32x4 v = p[i];
+      const u32x4 v = gload<u32x4>(row + 32 * c + 16 * i);
       q[4 * i] = v.x;
       q[4 * i + 1] = v.y;
       q[4 * i + 2] = v.z;
@@ -339,12 +348,11 @@ __device__ __forceinline__ void load_chunk(const uint8_t* row, int c, int row_wo
   } else if constexpr (BITS == 3) {
     // codes 32c.. start in word w0 = floor(32c/10) at code offset (32c mod 10);
     // the chunk touches at most 5 words (clamped to the row)
-    const uint32_t* w = (const uint32_t*)row;
     const int w0 = (32 * c) / 10;
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
       const int wi = w0 + i < row_words ? w0 + i : row_words - 1;
-      q[i] = w[wi];
+      q[i] = gload<uint32_t>(row + 4 * wi);
     }
   }
 }
@@ -491,7 +499,7 @@ __device__ __forceinline__ void load_rows(RowsQ<BITS, CPL, R>& Q, const uint8_t*
       const bool ok = rc[r] != nullptr && ch < nch;
       if (ok) {
         load_chunk<BITS>(rc[r], ch, row_words, Q.q[r][c]);
-        Q.sb[r][c] = rs[r][ch >> 1];
+        Q.sb[r][c] = gload<uint32_t>((const uint8_t*)(rs[r] + (ch >> 1)));
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) Q.q[r][c][i] = 0u;
@@ -500,17 +508,21 @@ __device__ __forceinline__ void load_rows(RowsQ<BITS, CPL, R>& Q, const uint8_t*
     }
 }
 
-// Marks the packed words as redefined (no instruction is emitted): keeps the
-// compiler from hoisting the unpacking of every row out of a loop over token
-// rows, which would hold all decoded pairs live at once.
+// Marks the packed words and scale/bias words as redefined (no instruction is
+// emitted): keeps the compiler from hoisting the unpacking of every row out of
+// a loop over token rows, which would hold all decoded pairs live at once, and
+// from hoisting the scale/bias arithmetic, which would wait for the weight
+// loads before the loop issues its input loads.
 template <int BITS, int CPL, int R>
 __device__ __forceinline__ void opaque(RowsQ<BITS, CPL, R>& Q) {
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int c = 0; c < CPL; ++c)
+    for (int c = 0; c < CPL; ++c) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(Q.q[r][c][i]));
+      asm volatile("" : "+v"(Q.sb[r][c]));
+    }
 }
 
 template <int BITS, int CPL, int R, int NX>
