@@ -21,6 +21,9 @@ row per step (seed 1000 + step). Prints one JSON line:
   counters read for a plain device copy of known size (--copy-probe), stored
   below with a hash of the kernel sources and reported only while the sources
   still hash the same;
+* step_us: median, 10th and 90th percentile of the per-step call durations
+  (the same HIP events); unique_experts_per_layer: the mean size of the union
+  of the rows' selected experts per layer and step;
 * cpu_baseline: the fp64 oracle timed on this host on a bounded sample.
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload a3b] [--no-cpu]
@@ -47,7 +50,7 @@ KERNEL_SOURCES = ["stack1.hip", "gemv.h", "device_common.h"]  # the stack kernel
 # 256 MiB device copy measured the same way. Keyed by workload; valid only
 # for the kernel sources whose hash is stored with it.
 TRAFFIC = {
-    "a3b": {"src_hash": "1b0eea5d7693d2c2", "fetch_bytes": 993_746_459, "write_bytes": 55_063_826},
+    "a3b": {"src_hash": "5d724e6e7bbda340", "fetch_bytes": 993_818_668, "write_bytes": 55_063_859},
 }
 
 
@@ -211,13 +214,16 @@ def main() -> int:
         ev[2 * s + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_s = float(np.mean([ev[2 * s].elapsed_time(ev[2 * s + 1]) for s in range(K)])) / 1e3
+    call_ms = np.array([ev[2 * s].elapsed_time(ev[2 * s + 1]) for s in range(K)])
+    launch_s = float(np.mean(call_ms)) / 1e3
     st = ds.status(T)
     if st != 0:
         print(f"stack kernel status {st}: a cross-workgroup wait timed out", file=sys.stderr)
         return 1
     ids_h = ids.cpu().numpy()
     tb = touched_bytes(w, ids_h)
+    # unique routed experts per layer and step (the union over the T rows)
+    units = np.array([len(np.unique(ids_h[s, l])) for s in range(K) for l in range(L)])
     tok_s = T * K / wall
     gbps = tb / (wall * 1e9)
     kernel_gbps = tb / K / launch_s / 1e9
@@ -251,6 +257,10 @@ def main() -> int:
             "touched_bytes_per_step": tb // K,
         },
         "achieved_GBps": round(gbps, 1),
+        "step_us": {"median": round(float(np.median(call_ms)) * 1e3, 1),
+                    "p10": round(float(np.percentile(call_ms, 10)) * 1e3, 1),
+                    "p90": round(float(np.percentile(call_ms, 90)) * 1e3, 1)},
+        "unique_experts_per_layer": round(float(units.mean()), 2),
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "roofline": {
             "bound": "hbm",
