@@ -551,11 +551,11 @@ template <int CPL, int RD>
 __global__ void __launch_bounds__(1024) down_kernel(Dims d, Ptrs p, int J) {
   down_body<CPL, RD>(d, p, J);
 }
-// up to 8 waves with 8 rows per lane group (J = 16 at K <= 1024): for many
-// token rows, where each unit's activations are read once per workgroup and
-// a wider slice halves those reads
+// up to 12 waves (three per SIMD, as its registers allow) with 8 rows per
+// lane group (J = 16 at K <= 1024): for many token rows, where each unit's
+// activations are read once per workgroup and a wider slice halves those reads
 template <int CPL, int RD>
-__global__ void __launch_bounds__(512) down_kernel_wide(Dims d, Ptrs p, int J) {
+__global__ void __launch_bounds__(768) down_kernel_wide(Dims d, Ptrs p, int J) {
   down_body<CPL, RD>(d, p, J);
 }
 
@@ -637,7 +637,7 @@ LayerPlan make_plan(const moe_shape_t& s, const moe_layer_layout_t& L, int T) {
   // down: J output rows per workgroup (about 256 workgroups), RD rows per lane
   // group for the longest K, with RD * chunks <= 4 to bound registers; from
   // 16 token rows on, one chunk per lane, a wide variant with RD = 8 and at
-  // most 8 waves (J up to 16)
+  // most 12 waves (J up to 16)
   const int rpw_min = 64 / lanes_per_row(d.imax);  // rows per pass of the longest K
   P.d_wide = T >= 16 && P.cpl_i == 1;
   const int rd_max = P.d_wide ? 8 : 4 / P.cpl_i;
@@ -654,7 +654,7 @@ LayerPlan make_plan(const moe_shape_t& s, const moe_layer_layout_t& L, int T) {
   }
   P.d_grid = (s.hidden + P.J - 1) / P.J;
   int nw = max_units + 1;
-  if (nw > (P.d_wide ? 8 : 16)) nw = P.d_wide ? 8 : 16;
+  if (nw > (P.d_wide ? 12 : 16)) nw = P.d_wide ? 12 : 16;
   P.d_threads = 64 * nw;
   P.mfma = T >= kMfmaMinT && s.router_bits == 8 && s.shared_bits == 8 && mfma_enabled();
   P.m_nt = T > 16 ? 2 : 1;
