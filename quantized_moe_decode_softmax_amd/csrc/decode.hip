@@ -123,12 +123,13 @@ template <int CPL>
 struct TaskRows {
   static constexpr int R = CPL >= 2 ? 2 : 4;  // rows loaded per lane group
 };
-// row pairs per lane group of one routed-expert task: more than the route
-// kernel's, so that a token row's arranged input serves several pairs and a
-// wave has more weight bytes in flight per task
+// row pairs per lane group of one routed-expert task: two with one chunk per
+// lane, so that a token row's arranged input serves several pairs and a wave
+// has more weight bytes in flight per task; one from two chunks per lane on,
+// where the registers of a second pair would cost a wave per SIMD
 template <int CPL>
 struct ExpertPairs {
-  static constexpr int RP = CPL >= 4 ? 1 : 2;
+  static constexpr int RP = CPL >= 2 ? 1 : 2;
 };
 
 // RMS factor and shared-expert gate of token row t (written once per call),
