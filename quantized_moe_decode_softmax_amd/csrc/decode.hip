@@ -330,11 +330,6 @@ __device__ __forceinline__ void swiglu_rows(const Dims& d, const Ptrs& p, int ta
   float r = 0.f;
   for (int task = task0; task < task1; ++task) {
     const int t = task / per_row, rem = task % per_row, slot = rem / tps, i0 = (rem % tps) * RP * rpw;
-    if (t != cur_t) {  // wave-uniform
-      prep_x<BITS, CPL>(x, p.h_in + (int64_t)t * d.H, d.H, li, lpr);
-      r = p.rinv[t];
-      cur_t = t;
-    }
     const int e = p.ids[t * d.k + slot];
     const uint8_t* gate = p.layer + d.off_e0 + (int64_t)e * d.e_stride;
     const uint8_t* up = gate + d.off_e_up;
@@ -354,6 +349,13 @@ __device__ __forceinline__ void swiglu_rows(const Dims& d, const Ptrs& p, int ta
     }
     RowsQ<BITS, CPL, R> Q;
     load_rows<BITS, CPL, R>(Q, rc, rs, d.H, (int)(rb >> 2), li, lpr);
+    // the token row's input after the weight loads are issued: both are in
+    // flight together (the input's arrangement waits for its load)
+    if (t != cur_t) {  // wave-uniform
+      prep_x<BITS, CPL>(x, p.h_in + (int64_t)t * d.H, d.H, li, lpr);
+      r = p.rinv[t];
+      cur_t = t;
+    }
     float out[R];
     dot_rows<BITS, CPL, R, 1>(Q, x, x, out);
 #pragma unroll
