@@ -330,6 +330,13 @@ __device__ __forceinline__ void swiglu_rows(const Dims& d, const Ptrs& p, int ta
   float r = 0.f;
   for (int task = task0; task < task1; ++task) {
     const int t = task / per_row, rem = task % per_row, slot = rem / tps, i0 = (rem % tps) * RP * rpw;
+    if constexpr (CPL >= 4) {  // input first: the other order spills at 4 chunks per lane
+      if (t != cur_t) {
+        prep_x<BITS, CPL>(x, p.h_in + (int64_t)t * d.H, d.H, li, lpr);
+        r = p.rinv[t];
+        cur_t = t;
+      }
+    }
     const int e = p.ids[t * d.k + slot];
     const uint8_t* gate = p.layer + d.off_e0 + (int64_t)e * d.e_stride;
     const uint8_t* up = gate + d.off_e_up;
@@ -351,7 +358,7 @@ __device__ __forceinline__ void swiglu_rows(const Dims& d, const Ptrs& p, int ta
     load_rows<BITS, CPL, R>(Q, rc, rs, d.H, (int)(rb >> 2), li, lpr);
     // the token row's input after the weight loads are issued: both are in
     // flight together (the input's arrangement waits for its load)
-    if (t != cur_t) {  // wave-uniform
+    if (CPL < 4 && t != cur_t) {  // wave-uniform
       prep_x<BITS, CPL>(x, p.h_in + (int64_t)t * d.H, d.H, li, lpr);
       r = p.rinv[t];
       cur_t = t;
