@@ -622,6 +622,59 @@ __device__ __forceinline__ void pair_rows(const Args& a, const Ctx& c, const Tas
   }
 }
 
+// A routed pair task held in registers: the lane's chunks of its gate and up
+// rows (row r0 + sr_h of each) and their scale/bias words.
+template <int BITS, int CPL>
+struct PairRegs {
+  uint32_t g[CPL][8], u[CPL][8], gs[CPL], us[CPL];
+};
+// Requests the task's words with global loads (no wait); rows past the task
+// and chunks past the row are zero.
+template <int BITS, int CPL>
+__device__ __forceinline__ void pair_load(const Ctx& c, const Task& t, PairRegs<BITS, CPL>& P) {
+  const int cb = code_bytes(BITS, c.H), sbw = c.H >> 6;
+  const int row = t.r0 + c.sr_h;
+  const bool ok = c.sr_h < t.n;
+  const uint8_t* g = t.mat + (int64_t)row * cb;
+  const uint8_t* u = t.mat + t.up + (int64_t)row * cb;
+  const int64_t sbo = matrix_codes_bytes(BITS, t.rows_total, c.H) + (int64_t)row * sbw * 4;
+#pragma unroll
+  for (int m = 0; m < CPL; ++m) {
+    const int ch = c.li_h + c.lpr_h * m;
+    if (ok && ch < (c.H >> 5)) {
+      load_chunk<BITS>(g, ch, cb >> 2, P.g[m]);
+      load_chunk<BITS>(u, ch, cb >> 2, P.u[m]);
+      P.gs[m] = gload<uint32_t>(t.mat + sbo + 4 * (ch >> 1));
+      P.us[m] = gload<uint32_t>(t.mat + t.up + sbo + 4 * (ch >> 1));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        P.g[m][i] = 0u;
+        P.u[m][i] = 0u;
+      }
+      P.gs[m] = 0u;
+      P.us[m] = 0u;
+    }
+  }
+}
+// pair_rows on a task held in registers (the same sums in the same order).
+template <int CPL_H, int CPL_I, int BITS>
+__device__ __forceinline__ void pair_rows_reg(const Args& a, const Ctx& c, const Task& t, const PairRegs<BITS, CPL_H>& P,
+                                            const XLane<BITS, CPL_H>& x, float r) {
+  float pg = 0.f, pu = 0.f;
+  if (c.sr_h < t.n) {
+#pragma unroll
+    for (int m = 0; m < CPL_H; ++m) pg += chunk_partial<BITS, 1>(P.g[m], P.gs[m], x.w[m], x.s[m], x.w[m], x.s[m]);
+#pragma unroll
+    for (int m = 0; m < CPL_H; ++m) pu += chunk_partial<BITS, 1>(P.u[m], P.us[m], x.w[m], x.s[m], x.w[m], x.s[m]);
+  }
+  const float gv = reduce_row(pg, c.lpr_h) * r;
+  const float uv = reduce_row(pu, c.lpr_h) * r;
+  if (c.sr_h < t.n && c.li_h == c.lpr_h - 1)
+    st_copies(a.x_a + (int64_t)t.slot * c.imax + a_word(t.r0 + c.sr_h, c.imax), c.a_cs, c.n_copy,
+              split_a(silu_mul(gv, uv)), c.ep);
+}
+
 // The task's rows of one expert's down projection: the activation vector is
 // split and arranged once, then each row group takes rows sr, sr + rpw, ...
 // KF: K when known at compile time (0: t.K).
@@ -835,16 +888,53 @@ __device__ __forceinline__ void shared_down_part(const Args& a, const Ctx& c) {
   }
 }
 
+// Routed pair tasks per wave that phase B holds in registers (when every wave
+// of the workgroup has at most this many)
+constexpr int kRegPairs = 2;
+
 template <int CPL_H, int CPL_I, int EB, int SB, int KI, int KS, int NV>
 __device__ __forceinline__ void phases_bc(const Args& a, const Ctx& c) {
   const int nb = n_b_tasks<CPL_H, CPL_I>(a, c), nc = n_c_tasks(a, c);
   // the wave's tasks: B tasks c.wave, c.wave + 8, ..., then C tasks likewise
-  const int mb = nb > c.wave ? (nb - c.wave + kWaves - 1) / kWaves : 0;
+  int mb = nb > c.wave ? (nb - c.wave + kWaves - 1) / kWaves : 0;
   const int mc = nc > c.wave ? (nc - c.wave + kWaves - 1) / kWaves : 0;
+  // uniform over the workgroup; compiled for one chunk per lane only (the
+  // registers of wider rows would make the kernel spill)
+  const bool reg_b = CPL_H == 1 && nb <= kRegPairs * kWaves;
+  if constexpr (CPL_H == 1) if (reg_b) {
+    // B from registers: the wave's routed pairs are requested at once with
+    // global loads (a burst of a few KB per wave arrives about twice as soon
+    // that way as through LDS), computed, and published; only then are the
+    // down rows of phase C streamed into the ring, so that no wait for the
+    // pairs also waits for them (both complete in issue order).
+    MOE_T1_BITS(EB, c.ebits, B, {
+      PairRegs<B, CPL_H> P0, P1;
+      Task t0, t1;
+      if (mb > 0) {
+        t0 = b_task<CPL_H, CPL_I>(a, c, c.wave);
+        pair_load<B, CPL_H>(c, t0, P0);
+      }
+      if (mb > 1) {
+        t1 = b_task<CPL_H, CPL_I>(a, c, c.wave + kWaves);
+        pair_load<B, CPL_H>(c, t1, P1);
+      }
+      XLane<B, CPL_H> x;
+      h_lane<B, CPL_H>(S.h, c.H, c.li_h, c.lpr_h, x);
+      if (mb > 0) pair_rows_reg<CPL_H, CPL_I, B>(a, c, t0, P0, x, S.r);
+      if (mb > 1) pair_rows_reg<CPL_H, CPL_I, B>(a, c, t1, P1, x, S.r);
+    });
+    mb = 0;
+  }
   const int m = mb + mc;
   auto task = [&](int j) {
     return j < mb ? b_task<CPL_H, CPL_I>(a, c, c.wave + kWaves * j) : c_task(a, c, c.wave + kWaves * (j - mb));
   };
+  bool exchanged = false;
+  if (reg_b) {  // phase B is done: publish before streaming phase C
+    publish_a(a, c);
+    shared_down_part<CPL_I, SB, KS>(a, c);
+    exchanged = true;
+  }
   const uint32_t base = lds_addr(S.ring[c.wave]);
   // batches of whole tasks in the two halves: tasks [bs, be), bn instructions
   int bs0 = 0, be0 = 0, bn0 = 0, bs1 = 0, be1 = 0, bn1 = 0;
@@ -864,7 +954,6 @@ __device__ __forceinline__ void phases_bc(const Args& a, const Ctx& c) {
   };
   fill(0, bs0, be0, bn0);
   fill(1, bs1, be1, bn1);
-  bool exchanged = false;
   int fetched = -1;  // slot whose activations this wave holds in S.a
   for (int b = 0;; ++b) {
     const int h = b & 1;
