@@ -1,5 +1,6 @@
 // One-row stack decode (T = 1) as one persistent kernel per up to 64 layers,
-// with every weight byte streamed into LDS by direct global-to-LDS loads.
+// with the weights streamed into LDS by direct global-to-LDS loads (except a
+// wave's few routed gate/up pairs, which arrive sooner through registers).
 //
 // At one token row a layer is a short chain of device-wide dependencies
 // (hidden state -> router logits -> top-k -> activations -> down projections
@@ -12,9 +13,13 @@
 // every earlier one). Here each wave instead streams the rows of its tasks
 // into a private LDS ring with gfx950's global_load_lds_dwordx4 (16 bytes per
 // lane, 1 KB per instruction, no registers), two halves deep, and computes a
-// batch of tasks from LDS while the next batch is in flight. The arithmetic of
-// every dot product is the one of the per-layer kernels (gemv.h), so results
-// are bitwise equal to them.
+// batch of tasks from LDS while the next batch is in flight. A burst of only
+// a few KB per wave is the exception: global loads into registers bring it in
+// about half the time, so a wave's routed pairs, when it has at most two,
+// take that path (with no direct LDS load of the wave in flight behind them,
+// since both complete in issue order). The arithmetic of every dot product is
+// the one of the per-layer kernels (gemv.h), so results are bitwise equal to
+// them.
 //
 // Exchange between workgroups: 64-bit words, payload | epoch << 32 (epoch =
 // layer in the launch + 1), device-scope relaxed stores and loads; a consumer
@@ -37,15 +42,17 @@
 //      flag releases the other waves; meanwhile the last wave loads the
 //      shared expert's down rows [j0, j0 + J) and their inputs (published in
 //      phase A) into LDS
-//   B  stream and compute this workgroup's range of routed row pairs
-//      (k experts x I pairs split evenly over the grid), storing each
-//      activation as it is computed, then set the workgroup's ready flag;
-//      each wave then waits for the flags of the workgroups that computed
-//      the slot of its down task and reads that activation vector into LDS
+//   B  load (registers, at most two per wave, else the ring) and compute
+//      this workgroup's range of routed row pairs (k experts x I pairs split
+//      evenly over the grid), storing each activation as it is computed,
+//      then set the workgroup's ready flag; each wave then waits for the
+//      flags of the workgroups that computed the slot of its down task and
+//      reads that activation vector into LDS
 //   C  the shared expert's down rows (one task per wave, while the ready
 //      flags are awaited), the down-projection rows [j0, j0 + J) of the k
-//      experts (weights streamed during B), combine in rank order, residual,
-//      bf16, publish the slice of h_{l+1}
+//      experts (weights streamed through the ring during B, or right after
+//      the ready flag when B used registers), combine in rank order,
+//      residual, bf16, publish the slice of h_{l+1}
 //
 // Buffer reuse: every workgroup publishes a slice of h in every layer. Logits,
 // activations and flags of layer l+1 are written only by workgroups that have
