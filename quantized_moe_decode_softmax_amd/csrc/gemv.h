@@ -662,8 +662,14 @@ __device__ __forceinline__ int wave_min_i(int v) {
 // round takes the wave maximum of the lanes' list heads; if several lanes hold
 // that key, the lowest index among them wins; the winner pops its head.
 // KF: k when known at compile time (0: k <= kMaxTopK at run time).
-template <int M, int KF = 0>
-__device__ __forceinline__ void topk_select(int (&key)[M], int k, int& lane_id, float& lane_w) {
+// on_round(i, id) runs on the whole wave as soon as round i has chosen its
+// expert (id wave-uniform), so a caller can hand out each rank early.
+struct NoRoundHook {
+  __device__ void operator()(int, int) const {}
+};
+template <int M, int KF = 0, class OnRound = NoRoundHook>
+__device__ __forceinline__ void topk_select(int (&key)[M], int k, int& lane_id, float& lane_w,
+                                            const OnRound& on_round = OnRound()) {
   constexpr int KMAX = KF ? KF : kMaxTopK;
   const int lane = threadIdx.x & 63;
   int idx[M];
@@ -705,6 +711,7 @@ __device__ __forceinline__ void topk_select(int (&key)[M], int k, int& lane_id, 
         key[M - 1] = INT_MIN;
         idx[M - 1] = INT_MAX;
       }
+      on_round(i, id);
       const float v = key_f(mx);
       if (i == 0) top = v;
       if (lane == i) {

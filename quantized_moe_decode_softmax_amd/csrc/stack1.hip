@@ -419,6 +419,9 @@ struct Shared {
   float w[kMaxTopK];
   float r, sg;
   uint32_t route_ep;  // epoch of the layer whose routing ids/w/r/sg hold
+  // expert of rank i as soon as the top-k has chosen it: epoch << 16 | id
+  // (S.r of the same layer is in place before the first of them)
+  uint32_t rank_tag[kMaxTopK];
   uint32_t logit_ep;  // epoch of the layer whose logits wave 0 has seen (so all phase A output exists)
   __attribute__((aligned(16))) uint8_t ring[kWaves][kRingBytes];
   __attribute__((aligned(16))) uint8_t sd[kRingBytes];  // the shared expert's down rows of the slice
@@ -492,8 +495,9 @@ __device__ __forceinline__ int n_b_tasks(const Args& a, const Ctx& c) {
   }
   return n;
 }
-template <int CPL_H, int CPL_I>
-__device__ __forceinline__ Task b_task(const Args& a, const Ctx& c, int i) {
+// IdOf: the expert id of a rank (S.ids once the routing is complete).
+template <int CPL_H, int CPL_I, class IdOf>
+__device__ __forceinline__ Task b_task(const Args& a, const Ctx& c, int i, const IdOf& id_of) {
   const int f0 = blockIdx.x * c.pb, f1 = min(c.k * c.I, f0 + c.pb);
   Task t;
   t.kind = kRoutedPair;
@@ -507,7 +511,7 @@ __device__ __forceinline__ Task b_task(const Args& a, const Ctx& c, int i) {
     if (i < nt) {
       const int u = f / c.I;
       t.slot = u;
-      t.mat = c.layer + c.off_e0 + (int64_t)S.ids[u] * c.e_stride;
+      t.mat = c.layer + c.off_e0 + (int64_t)id_of(u) * c.e_stride;
       t.r0 = f % c.I + i * c.rpw_h;
       t.n = min(c.rpw_h, end - (f + i * c.rpw_h));
       break;
@@ -517,6 +521,18 @@ __device__ __forceinline__ Task b_task(const Args& a, const Ctx& c, int i) {
   }
   t.bytes = task_bytes(t.bits, t.K, t.n, true);
   return t;
+}
+template <int CPL_H, int CPL_I>
+__device__ __forceinline__ Task b_task(const Args& a, const Ctx& c, int i) {
+  return b_task<CPL_H, CPL_I>(a, c, i, [](int u) { return S.ids[u]; });
+}
+// The expert of rank u once wave 0's top-k has chosen it (this layer's tag).
+// On a time-out the stale id is still a valid expert (the status word says so).
+__device__ __forceinline__ int rank_id(const Args& a, const Ctx& c, int u) {
+  uint32_t spins = 0, v;
+  while (((v = *(volatile const uint32_t*)&S.rank_tag[u]) >> 16) != c.ep)
+    if (give_up(spins, a.status)) break;
+  return (int)(v & 0xFFFFu);
 }
 
 // ---- phase C tasks: for each slot (k routed experts in rank order, then
@@ -775,6 +791,8 @@ __device__ __forceinline__ void route(const Args& a, const Ctx& c, const uint32_
   // row group 0's last c.lane holds the sums
   const float r = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rms_factor(ss, c.H, c.eps)), c.lpr_h - 1));
   gd = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gd), c.lpr_h - 1));
+  if (c.lane == 0) S.r = r;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // S.r in place before any rank tag
   uint32_t rv[M];
   uint32_t want = 0u;
 #pragma unroll
@@ -786,15 +804,15 @@ __device__ __forceinline__ void route(const Args& a, const Ctx& c, const uint32_
   for (int m = 0; m < M; ++m) key[m] = c.lane + 64 * m < c.E ? fkey(r * __uint_as_float(rv[m])) : INT_MIN;
   int my_id;
   float my_w;
-  topk_select<M, KF>(key, c.k, my_id, my_w);
+  const uint32_t ep = c.ep;
+  topk_select<M, KF>(key, c.k, my_id, my_w, [ep](int i, int id) {
+    if ((threadIdx.x & 63) == 0) *(volatile uint32_t*)&S.rank_tag[i] = ep << 16 | (uint32_t)id;
+  });
   if (c.lane < c.k) {
     S.ids[c.lane] = my_id;
     S.w[c.lane] = my_w;
   }
-  if (c.lane == 0) {
-    S.r = r;
-    S.sg = 1.0f / (1.0f + expf(-(r * gd)));
-  }
+  if (c.lane == 0) S.sg = 1.0f / (1.0f + expf(-(r * gd)));
 }
 
 // ---- activations: this workgroup's ready flag, once every wave has stored
@@ -908,7 +926,11 @@ __device__ __forceinline__ void phases_bc(const Args& a, const Ctx& c) {
   // uniform over the workgroup; compiled for one chunk per lane only (the
   // registers of wider rows would make the kernel spill)
   const bool reg_b = CPL_H == 1 && nb <= kRegPairs * kWaves;
+  // the register path needs only the ids of its own ranks (as each is
+  // chosen); everything else waits for wave 0's complete routing
+  if (!reg_b) wait_lds_epoch(&S.route_ep, c.ep, a.status);
   if constexpr (CPL_H == 1) if (reg_b) {
+    auto id_of = [&](int u) { return rank_id(a, c, u); };
     // B from registers: the wave's routed pairs are requested at once with
     // global loads (a burst of a few KB per wave arrives about twice as soon
     // that way as through LDS), computed, and published; only then are the
@@ -918,11 +940,11 @@ __device__ __forceinline__ void phases_bc(const Args& a, const Ctx& c) {
       PairRegs<B, CPL_H> P0, P1;
       Task t0, t1;
       if (mb > 0) {
-        t0 = b_task<CPL_H, CPL_I>(a, c, c.wave);
+        t0 = b_task<CPL_H, CPL_I>(a, c, c.wave, id_of);
         pair_load<B, CPL_H>(c, t0, P0);
       }
       if (mb > 1) {
-        t1 = b_task<CPL_H, CPL_I>(a, c, c.wave + kWaves);
+        t1 = b_task<CPL_H, CPL_I>(a, c, c.wave + kWaves, id_of);
         pair_load<B, CPL_H>(c, t1, P1);
       }
       XLane<B, CPL_H> x;
@@ -1120,6 +1142,7 @@ __global__ void __launch_bounds__(kThreads) stack1_kernel(Args a) {
   c.sr_h = c.lane / c.lpr_h;
   c.cp = blockIdx.x % c.n_copy;
   if (threadIdx.x == 0) S.route_ep = S.logit_ep = 0u;  // ordered before their readers by the first barrier below
+  if (threadIdx.x < kMaxTopK) S.rank_tag[threadIdx.x] = 0u;
   for (int l = 0; l < a.n_layers; ++l) {
     c.layer = a.layers[l];
     c.ep = (uint32_t)l + 1;
@@ -1160,8 +1183,7 @@ __global__ void __launch_bounds__(kThreads) stack1_kernel(Args a) {
       shared_down_fetch<SH::NV>(a, c);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // phase A ring reads done
-    wait_lds_epoch(&S.route_ep, c.ep, a.status);  // wave 0's routing is in LDS
-    if (blockIdx.x == 0 && threadIdx.x < c.k) {
+    if (blockIdx.x == 0 && threadIdx.x < c.k) {  // wave 0, whose routing is complete
       if (a.ids_out) a.ids_out[(int64_t)l * c.k + threadIdx.x] = S.ids[threadIdx.x];
       if (a.w_out) a.w_out[(int64_t)l * c.k + threadIdx.x] = S.w[threadIdx.x];
     }
