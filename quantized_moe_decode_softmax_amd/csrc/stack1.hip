@@ -495,6 +495,26 @@ __device__ __forceinline__ int n_b_tasks(const Args& a, const Ctx& c) {
   }
   return n;
 }
+// Split order (one pair per task, 2 x kWaves pairs per workgroup, k even,
+// every workgroup a full share): workgroup g owns pairs [g pb/2, (g+1) pb/2)
+// of the first k/2 ranks and the same range of the last k/2 ranks, so each
+// wave's first pair is of an early rank and its second of a late one; the
+// first is computed while the second, requested once the top-k reaches its
+// rank, is still arriving.
+__device__ __forceinline__ bool split_b(const Ctx& c) {
+  return c.rpw_h == 1 && (c.k & 1) == 0 && c.pb == 2 * kWaves && c.nwg * c.pb == c.k * c.I && c.I <= 64 * c.pb;
+}
+// The workgroups whose ready flags cover the activations of routed slot u.
+__device__ __forceinline__ void slot_producers(const Ctx& c, int u, int& w0, int& w1) {
+  if (split_b(c)) {
+    const int h = c.pb / 2, base = u < c.k / 2 ? 0 : c.k / 2 * c.I;
+    w0 = (u * c.I - base) / h;
+    w1 = ((u + 1) * c.I - 1 - base) / h;
+  } else {
+    w0 = u * c.I / c.pb;
+    w1 = ((u + 1) * c.I - 1) / c.pb;
+  }
+}
 // IdOf: the expert id of a rank (S.ids once the routing is complete).
 template <int CPL_H, int CPL_I, class IdOf>
 __device__ __forceinline__ Task b_task(const Args& a, const Ctx& c, int i, const IdOf& id_of) {
@@ -505,6 +525,17 @@ __device__ __forceinline__ Task b_task(const Args& a, const Ctx& c, int i, const
   t.bits = c.ebits;
   t.rows_total = c.I;
   t.up = c.off_e_up;
+  if (split_b(c)) {
+    const int h = c.pb / 2;
+    const int f = i < h ? blockIdx.x * h + i : c.k / 2 * c.I + blockIdx.x * h + (i - h);
+    const int u = f / c.I;
+    t.slot = u;
+    t.mat = c.layer + c.off_e0 + (int64_t)id_of(u) * c.e_stride;
+    t.r0 = f % c.I;
+    t.n = 1;
+    t.bytes = task_bytes(t.bits, t.K, t.n, true);
+    return t;
+  }
   for (int f = f0; f < f1;) {
     const int end = min(f1, (f / c.I + 1) * c.I);
     const int nt = (end - f + c.rpw_h - 1) / c.rpw_h;
@@ -850,7 +881,8 @@ __device__ __forceinline__ void fetch_a(const Args& a, const Ctx& c, int slot) {
 #pragma unroll
       for (int j = 0; j < NV; ++j) sv[j] = (want >> j & 1u) ? ld_tag(src + off(j)) : 0ull;
     }
-    const int w0 = slot * c.I / c.pb, w1 = ((slot + 1) * c.I - 1) / c.pb;
+    int w0, w1;
+    slot_producers(c, slot, w0, w1);
     uint32_t fv[2];
     const uint32_t fwant = (w0 + c.lane <= w1 ? 1u : 0u) | (w0 + c.lane + 64 <= w1 ? 2u : 0u);
     poll<2>(a.x_flag + c.cp * 512 + w0 + c.lane, [](int m) { return (int64_t)64 * m; }, fwant, c.ep, fv, a.status);
