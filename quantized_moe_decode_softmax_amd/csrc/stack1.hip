@@ -165,6 +165,17 @@ __device__ __forceinline__ void poll(const uint64_t* p, const Off& off, uint32_t
   }
 }
 
+// LDS words that one wave sets and others wait for: relaxed workgroup-scope
+// atomics, which compile to plain ds_write / ds_read. (A volatile access
+// through the generic pointer becomes a flat access, and the compiler then
+// waits for every outstanding global load of the wave as well.)
+__device__ __forceinline__ uint32_t lds_ld(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_st(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
 // Workgroup barrier for LDS data only (the kernel never reads its own global
 // stores through a barrier, so it does not wait for them as __syncthreads does).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -561,7 +572,7 @@ __device__ __forceinline__ Task b_task(const Args& a, const Ctx& c, int i) {
 // On a time-out the stale id is still a valid expert (the status word says so).
 __device__ __forceinline__ int rank_id(const Args& a, const Ctx& c, int u) {
   uint32_t spins = 0, v;
-  while (((v = *(volatile const uint32_t*)&S.rank_tag[u]) >> 16) != c.ep)
+  while (((v = lds_ld(&S.rank_tag[u])) >> 16) != c.ep)
     if (give_up(spins, a.status)) break;
   return (int)(v & 0xFFFFu);
 }
@@ -829,7 +840,7 @@ __device__ __forceinline__ void route(const Args& a, const Ctx& c, const uint32_
 #pragma unroll
   for (int m = 0; m < M; ++m) want |= (c.lane + 64 * m < c.E ? 1u : 0u) << m;
   poll<M>(a.x_logit + c.cp * c.l_cs + c.lane, [](int m) { return (int64_t)64 * m; }, want, c.ep, rv, a.status);
-  *(volatile uint32_t*)&S.logit_ep = c.ep;
+  lds_st(&S.logit_ep, c.ep);
   int key[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) key[m] = c.lane + 64 * m < c.E ? fkey(r * __uint_as_float(rv[m])) : INT_MIN;
@@ -837,7 +848,7 @@ __device__ __forceinline__ void route(const Args& a, const Ctx& c, const uint32_
   float my_w;
   const uint32_t ep = c.ep;
   topk_select<M, KF>(key, c.k, my_id, my_w, [ep](int i, int id) {
-    if ((threadIdx.x & 63) == 0) *(volatile uint32_t*)&S.rank_tag[i] = ep << 16 | (uint32_t)id;
+    if ((threadIdx.x & 63) == 0) lds_st(&S.rank_tag[i], ep << 16 | (uint32_t)id);
   });
   if (c.lane < c.k) {
     S.ids[c.lane] = my_id;
@@ -915,7 +926,7 @@ __device__ __forceinline__ void fetch_a(const Args& a, const Ctx& c, int slot) {
 // Waits until LDS word *p holds epoch (set by another wave of the workgroup).
 __device__ __forceinline__ void wait_lds_epoch(const uint32_t* p, uint32_t epoch, uint32_t* status) {
   uint32_t spins = 0;
-  while (*(volatile const uint32_t*)p != epoch)
+  while (lds_ld(p) != epoch)
     if (give_up(spins, status)) break;
   asm volatile("" ::: "memory");
 }
@@ -1210,7 +1221,7 @@ __global__ void __launch_bounds__(kThreads) stack1_kernel(Args a) {
       }
     }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // routing stored before its flag
-      *(volatile uint32_t*)&S.route_ep = c.ep;
+      lds_st(&S.route_ep, c.ep);
     } else if (c.wave == kWaves - 1) {
       shared_down_fetch<SH::NV>(a, c);
     }
