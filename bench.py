@@ -28,6 +28,9 @@ row per step (seed 1000 + step). Prints one JSON line:
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload a3b] [--no-cpu]
        python bench.py --copy-probe MIB   (PMC calibration: 5 device copies)
+       python bench.py --phase-trace      (the phase-trace build libmoe_trace.so: per-phase
+                                           timestamps of the streaming stack kernel, T = 1;
+                                           prints a table, no JSON line)
 """
 
 from __future__ import annotations
@@ -160,6 +163,78 @@ def cpu_baseline(w, budget_s: float = 15.0):
     }
 
 
+PHASES = ["layer start", "h staged", "phase A computed", "all logits seen", "top-k done",
+          "routed loads issued", "routed pairs computed (wave 0)", "routed pairs computed (wave 7)",
+          "activations published", "first down inputs in LDS", "down rows done", "combine done",
+          "shared down inputs fetched (wave 7)"]
+
+
+def phase_trace(w, K: int, W: int) -> int:
+    """Per-phase timestamps of the streaming stack kernel (phase-trace build only)."""
+    import ctypes
+
+    import torch
+
+    from quantized_moe_decode_softmax_amd import _lib as Lb
+    from quantized_moe_decode_softmax_amd.build import TRACE_LIB
+
+    Lb.use_library(TRACE_LIB)
+    from quantized_moe_decode_softmax_amd.runtime import DeviceStack
+
+    if w.T != 1:
+        print("--phase-trace covers the one-row streaming kernel (T = 1)", file=sys.stderr)
+        return 2
+    ds = DeviceStack.from_workload(w)
+    f = Lb.lib().moe_phase_trace_offset
+    f.argtypes = [ctypes.POINTER(Lb.moe_shape_t), ctypes.c_int32]
+    f.restype = ctypes.c_int64
+    off = f(ctypes.byref(ds.shape), 1)
+    if off < 0:
+        print("this library build records no phase timestamps", file=sys.stderr)
+        return 2
+    L, n_ph = w.n_layers, 16
+    region = ds.ws[off:off + 64 * 512 * n_ph * 8].view(torch.int64).view(64, 512, n_ph)
+    st = ds.state()
+    stream = torch.cuda.current_stream().cuda_stream
+    out = torch.empty((1, w.hidden), dtype=torch.bfloat16, device="cuda")
+    xs = [ds.rows(1000 + s, 1) for s in range(W + K)]
+    recs = []
+    for s in range(W + K):
+        region.zero_()
+        Lb.moe_stack_decode(st, 1, xs[s].data_ptr(), out.data_ptr(), None, None, None, stream)
+        if s >= W:
+            recs.append(region[:L].clone())
+    torch.cuda.synchronize()
+    if ds.status(1) != 0:
+        print("a cross-workgroup wait timed out", file=sys.stderr)
+        return 1
+    r = torch.stack(recs).cpu().numpy()  # [K, 64, 512, 16]
+    used = r[:, :, :, 0].any(axis=(0, 1))
+    nwg = int(used.sum())
+    r = r[:, :, :nwg].astype(np.float64)
+    t0 = r[:, :, :, 0].min(axis=2, keepdims=True)  # earliest layer start over workgroups
+    rel = (r - t0[..., None]) * 0.01  # 100 MHz ticks -> us
+    valid = r > 0
+    lay = slice(2, L)  # skip the first layers (cold start)
+    print(f"phase timestamps, {w.name} T=1: {K} steps x layers {lay.start}..{L - 1} x {nwg} workgroups "
+          f"(us after the earliest workgroup started the layer)")
+    print(f"{'slot':>4} {'phase':<38} {'p10':>7} {'median':>7} {'p90':>7} {'max':>7}")
+    rows = []
+    for p, name in enumerate(PHASES):
+        v = rel[:, lay, :, p][valid[:, lay, :, p]]
+        if v.size == 0:
+            continue
+        q = np.percentile(v, [10, 50, 90]).tolist() + [float(v.max())]
+        rows.append((p, name, q))
+        print(f"{p:>4} {name:<38} {q[0]:7.2f} {q[1]:7.2f} {q[2]:7.2f} {q[3]:7.2f}")
+    # layer duration: next layer's earliest start - this layer's earliest start
+    starts = r[:, :L, :, 0].min(axis=2) * 0.01
+    dur = np.diff(starts, axis=1)[:, lay.start:]
+    print(f"layer duration (earliest start to earliest start): median {np.median(dur):.2f} us, "
+          f"p10 {np.percentile(dur, 10):.2f}, p90 {np.percentile(dur, 90):.2f}")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +245,7 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
     ap.add_argument("--rows", type=int, default=0, help="token rows per step (default: the workload's T)")
+    ap.add_argument("--phase-trace", action="store_true", help="per-phase timestamps (phase-trace build)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding of this "
@@ -177,6 +253,10 @@ def main() -> int:
         return 2
     if args.copy_probe:
         return copy_probe(args.copy_probe)
+    if args.phase_trace:
+        from quantized_moe_decode_softmax_amd import WORKLOADS as _W
+
+        return phase_trace(_W[args.workload], min(args.steps, 50), min(args.warmup, 10))
 
     import torch
 
@@ -196,12 +276,11 @@ def main() -> int:
     out = torch.empty((T, w.hidden), dtype=torch.bfloat16, device="cuda")
     from quantized_moe_decode_softmax_amd import _lib as Lb
 
-    ptrs = [b.data_ptr() for b in ds.layers]
     stream = torch.cuda.current_stream().cuda_stream
+    st = ds.state()  # moe_stack_init: the descriptor table of the 40 layers in the workspace, once
 
     def step(x, idp, wp):
-        Lb.moe_decode_stack(ds.shape, ptrs, T, x.data_ptr(), out.data_ptr(), idp, wp, None, ds.ws.data_ptr(),
-                            ds.ws_bytes, stream)
+        Lb.moe_stack_decode(st, T, x.data_ptr(), out.data_ptr(), idp, wp, None, stream)
 
     for s in range(W):
         step(xs[s], ids[0].data_ptr(), wts[0].data_ptr())

@@ -25,10 +25,15 @@
  *     failed validation launches nothing and touches no buffer.
  *   - "dev" pointers are device (HBM) addresses, "host" pointers host
  *     addresses. The caller owns every buffer; the library never allocates
- *     device memory and keeps no pointer beyond a call.
+ *     device memory. It keeps no pointer beyond a call, except that
+ *     moe_stack_init writes a descriptor table of layer pointers into the
+ *     caller's workspace and fills a caller-owned moe_stack_t.
  *   - launches are asynchronous on the given stream (a hipStream_t, NULL =
  *     the default stream); device-side faults surface at the caller's next
- *     synchronisation.
+ *     synchronisation. With MOE_DEBUG_SYNC=1 in the environment (read once,
+ *     at the first call), every entry point that launches work waits for its
+ *     stream before returning and turns a HIP error into MOE_ERR_HIP, and a
+ *     stack call whose bounded waits timed out returns MOE_ERR_TIMEOUT.
  *   - results are bitwise deterministic, and for T <= 8 row t of a T-row
  *     call is bitwise equal to a T = 1 call on that row alone.
  */
@@ -50,13 +55,18 @@ enum {
   MOE_ERR_UNSUPPORTED = -2,     /* bit width / group / dimension not supported */
   MOE_ERR_ALIGNMENT = -3,       /* device pointer not aligned as documented */
   MOE_ERR_WORKSPACE = -4,       /* workspace smaller than moe_workspace_bytes() */
-  MOE_ERR_HIP = -5              /* a HIP runtime call failed */
+  MOE_ERR_HIP = -5,             /* a HIP runtime call failed */
+  MOE_ERR_TIMEOUT = -6          /* (MOE_DEBUG_SYNC only) a bounded cross-workgroup wait timed out */
 };
 
 /* Shape of one MoE layer. Limits: hidden, inter, shared_inter multiples of 64
  * in [64, 8192]; 1 <= top_k <= min(n_experts, 16); n_experts <= 512;
  * expert_bits, shared_bits in {2, 3, 4, 6, 8}; router_bits in {2, 3, 4, 6, 8}
- * or 16 (dense bf16 router); group must be 64; rms_eps > 0. */
+ * or 16 (dense bf16 router); group must be 64; rms_eps > 0.
+ * The fields follow the PureDrive card, "Summary" (256 experts, top-8 plus a
+ * shared expert, 6-bit experts and 8-bit shared expert/router) and the
+ * flash-moe news page, "Model architecture" (512 experts, hidden 4096) and
+ * "FMA-optimised dequant kernel" (group-affine 4-bit and 2-bit weights). */
 typedef struct moe_shape {
   int32_t hidden;        /* H */
   int32_t n_experts;     /* E routed experts */
@@ -96,6 +106,7 @@ typedef struct moe_shape {
  *                  halves); bits 15 and 31 zero; each row padded to whole
  *                  dwords with zero.
  * row_bytes = cols*bits/8 for bits 2/4/6/8, 4*ceil(cols/10) for bits 3.
+ * Returns the block's bytes, or a negative MOE_ERR_* code.
  */
 int64_t moe_matrix_bytes(int32_t bits, int32_t rows, int32_t cols);
 
@@ -103,7 +114,9 @@ int64_t moe_matrix_bytes(int32_t bits, int32_t rows, int32_t cols);
  * router (packed matrix [E, H], or dense bf16 [E, H] when router_bits = 16),
  * gate vector (bf16 [H]), shared expert, then routed expert e at
  * expert0 + e * expert_stride. An expert is three packed matrices back to
- * back: gate [I, H], up [I, H], down [H, I]. */
+ * back: gate [I, H], up [I, H], down [H, I]. One contiguous block per expert
+ * is what the flash-moe news page, "SSD Expert Streaming", reads per selected
+ * expert (about 6.75 MB at the 397B shape, 4-bit). */
 typedef struct moe_layer_layout {
   int64_t router;
   int64_t gatevec;
@@ -117,60 +130,84 @@ typedef struct moe_layer_layout {
   int64_t total_bytes;    /* whole layer block */
 } moe_layer_layout_t;
 
-/* Validates the shape (pure host code). */
+/* Validates the shape (pure host code, no device). */
 int32_t moe_validate_shape(const moe_shape_t* shape);
 
-/* Fills *out for a valid shape. */
+/* Validates the shape and a row count 1 <= T <= 32 (pure host code, no
+ * device). T is the number of token rows of one call: 1 for decode, up to 8
+ * for the verify pass of the PureDrive card, "How it works" (3 rows there),
+ * up to 32 for batches. */
+int32_t moe_validate(const moe_shape_t* shape, int32_t T);
+
+/* Fills *out (host) for a valid shape. */
 int32_t moe_layer_layout(const moe_shape_t* shape, moe_layer_layout_t* out);
 
-/* Bytes of workspace a decode call with up to T rows needs (1 <= T <= 32).
- * The same workspace serves moe_decode_layer and moe_decode_stack. Returns a
- * negative MOE_ERR_* code for an invalid shape or T. */
-int64_t moe_workspace_bytes(const moe_shape_t* shape, int32_t T);
+/* Bytes of one routed expert block (gate, up and down packed matrices with
+ * their padding; the layout's expert_stride), e.g. 7,077,888 = 6.75 MiB at
+ * the 397B shape with 4-bit codes (flash-moe news page, "SSD Expert
+ * Streaming": about 6.75 MB per expert). Negative MOE_ERR_* on a bad shape. */
+int64_t moe_expert_bytes(const moe_shape_t* shape);
+
+/* Bytes of one whole layer block (router, gate vector, shared expert and all
+ * routed experts). Negative MOE_ERR_* on a bad shape. */
+int64_t moe_layer_bytes(const moe_shape_t* shape);
+
+/* Bytes of workspace for calls of up to T rows (1 <= T <= 32) on stacks of
+ * up to n_layers layers (n_layers = 0: moe_decode_layer and moe_decode_stack
+ * only; n_layers >= 1 adds the descriptor table moe_stack_init writes). The
+ * same workspace serves every decode entry point. Negative MOE_ERR_* on an
+ * invalid shape, T or n_layers (0 <= n_layers <= 4096). */
+int64_t moe_workspace_bytes(const moe_shape_t* shape, int32_t n_layers, int32_t T);
 
 /* Host-side packing of one matrix into the layout above.
  * codes_host: uint8 [rows, cols], each < 2^bits; scale_host, bias_host: bf16
  * bit patterns [rows, cols/64]; dst_host: moe_matrix_bytes() bytes, fully
  * written (padding zero). cols must be a multiple of 64. A code >= 2^bits
- * returns MOE_ERR_INVALID_ARG with dst partly written. */
+ * returns MOE_ERR_INVALID_ARG with dst partly written. The group-affine form
+ * is the flash-moe news page's, "FMA-optimised dequant kernel". */
 int32_t moe_pack_matrix(int32_t bits, int32_t rows, int32_t cols, const uint8_t* codes_host,
                         const uint16_t* scale_host, const uint16_t* bias_host, void* dst_host);
 
-/* Inverse of moe_pack_matrix (host only). */
+/* Inverse of moe_pack_matrix (host only; same arguments, outputs written). */
 int32_t moe_unpack_matrix(int32_t bits, int32_t rows, int32_t cols, const void* src_host,
                           uint8_t* codes_host, uint16_t* scale_host, uint16_t* bias_host);
 
 /*
  * Synthetic weights: writes the whole layer block of layer `layer` on the
- * device (layer_dev: moe_layer_layout().total_bytes bytes, 256-byte aligned),
- * drawing codes, bf16 scales/biases and bf16 vectors from the seeded
- * splitmix64 counter generator (Steele, Lea & Flood, OOPSLA 2014) with
- * per-(layer, expert) sub-seeds. The definition of the draws is the one
- * documented with the library sources (gen kernels).
+ * device (layer_dev: moe_layer_bytes() bytes, 256-byte aligned), drawing
+ * codes, bf16 scales/biases and bf16 vectors from the seeded splitmix64
+ * counter generator (Steele, Lea & Flood, OOPSLA 2014) with per-(layer,
+ * expert) sub-seeds. The pages publish no weights (PureDrive card: the
+ * repository holds documentation only); the definition of the draws is the
+ * one documented with the library sources (gen kernels).
  */
 int32_t moe_generate_layer(const moe_shape_t* shape, uint64_t seed, int32_t layer, void* layer_dev,
                            moe_stream_t stream);
 
 /* Synthetic x rows: bf16 [T, H] ~ N(0, 1) from seed_x, written to out_dev
- * (16-byte aligned). */
+ * (16-byte aligned), as the generator above. */
 int32_t moe_generate_rows(uint64_t seed_x, int32_t T, int32_t H, uint16_t* out_dev, moe_stream_t stream);
 
 /*
- * One MoE layer on T rows (1 <= T <= 32).
+ * One MoE layer on T rows (1 <= T <= 32): the whole step of the header
+ * comment, i.e. the router GEMV, softmax top-k, the selected experts' and the
+ * shared expert's dequantised SwiGLU GEMVs and the combine + residual + gate
+ * of the flash-moe news page, "Metal Compute Shaders" and "Deferred GPU
+ * Expert Compute", with only the router-selected experts read (AiiStream
+ * news page: the router's choice decides which experts are loaded).
  *   layer_dev : layer block (layout above), 256-byte aligned
  *   h_in_dev  : bf16 [T, H], 16-byte aligned; h_out_dev: bf16 [T, H], 16-byte
  *               aligned, must not overlap h_in_dev
  *   ids_dev   : int32 [T, k] selected experts (descending logit) or NULL
  *   w_dev     : float [T, k] renormalised routing weights or NULL
- *   ws_dev    : workspace of ws_bytes >= moe_workspace_bytes(shape, T),
+ *   ws_dev    : workspace of ws_bytes >= moe_workspace_bytes(shape, 0, T),
  *               256-byte aligned; contents need no initialisation.
  * Calls that share one workspace must be ordered on one stream.
  * Rows are independent. For T <= 8 (the verify batch of the PureDrive card,
  * "How it works") row t of the result is bitwise equal to a one-row call on
  * row t. For T > 8 with an 8-bit router and shared expert, those two run on
  * the bf16 matrix cores (different fp32 summation order; rows agree with the
- * one-row result to rounding, not bit for bit); MOE_MFMA=0 in the environment
- * keeps them on the vector-unit kernels.
+ * one-row result to rounding, not bit for bit).
  */
 int32_t moe_decode_layer(const moe_shape_t* shape, const void* layer_dev, int32_t T, const uint16_t* h_in_dev,
                          uint16_t* h_out_dev, int32_t* ids_dev, float* w_dev, void* ws_dev, size_t ws_bytes,
@@ -178,27 +215,80 @@ int32_t moe_decode_layer(const moe_shape_t* shape, const void* layer_dev, int32_
 
 /*
  * A stack of n_layers MoE layers with distinct weights: h_0 = h_in,
- * h_{l+1} = bf16(layer_l(h_l)), h_out = h_{n_layers}. The host never waits
- * inside the stack. For T = 1 each group of up to 64 layers runs as one
- * kernel with one workgroup per compute unit whose workgroups wait on each
- * other's results (bounded waits; see moe_stack_status); other calls run as
- * kernels per layer (the same as moe_decode_layer). Both give the same
- * results bit for bit.
+ * h_{l+1} = bf16(layer_l(h_l)), h_out = h_{n_layers}. Each layer's combined
+ * output is handed to the next layer on the GPU (flash-moe news page,
+ * "Deferred GPU Expert Compute"), and no host work or per-layer submission
+ * sits between layers (the per-layer command-buffer gap the M5 Max news page,
+ * "Effective optimisations", removes by pre-encoding). For T = 1 each group
+ * of up to 64 layers runs as one kernel with one workgroup per compute unit,
+ * whose workgroups wait on each other's results (bounded waits; see
+ * moe_stack_status); it is launched only when the device can hold all its
+ * workgroups at once, else the call runs as kernels per layer (the same as
+ * moe_decode_layer). Both give the same results bit for bit.
  *   layers_host : host array of n_layers device pointers to layer blocks
+ *                 (read during the call only)
  *   ids_dev     : int32 [n_layers, T, k] or NULL; w_dev: float [n_layers, T, k] or NULL
  *   h_trace_dev : bf16 [n_layers + 1, T, H] (h_0 .. h_L) or NULL
+ *   ws_dev      : ws_bytes >= moe_workspace_bytes(shape, 0, T)
  * Other arguments as for moe_decode_layer.
  */
 int32_t moe_decode_stack(const moe_shape_t* shape, const void* const* layers_host, int32_t n_layers, int32_t T,
                          const uint16_t* h_in_dev, uint16_t* h_out_dev, int32_t* ids_dev, float* w_dev,
                          uint16_t* h_trace_dev, void* ws_dev, size_t ws_bytes, moe_stream_t stream);
 
+/* Path selection of an initialised stack (moe_stack_init flags). */
+enum {
+  MOE_PATH_DEFAULT = 0,
+  MOE_PATH_PER_LAYER = 1,  /* T = 1 calls also run as kernels per layer (no persistent kernel) */
+  MOE_PATH_NO_MFMA = 2     /* batches of T > 8 keep the router and shared expert on the vector units */
+};
+
+/* State of an initialised stack: plain host data owned by the caller (may be
+ * copied); filled by moe_stack_init, read by moe_stack_decode. */
+typedef struct moe_stack {
+  moe_shape_t shape;
+  int32_t n_layers;
+  int32_t t_max;
+  int32_t flags;
+  uint32_t magic;        /* set by moe_stack_init */
+  void* ws_dev;
+  size_t ws_bytes;
+  int64_t table_offset;  /* bytes from ws_dev to the descriptor table */
+  int64_t reserved[4];
+} moe_stack_t;
+
 /*
- * Reads the status word the last moe_decode_stack call on this workspace
- * left (waits for the stream first): 0 = every cross-workgroup wait was met;
- * 1 = a wait timed out (about a second without progress, e.g. when other
- * work kept part of the stack kernel's workgroups off the device), the call's
- * outputs are then invalid. T must be the T of that call.
+ * Prepares repeated decoding of one stack (the stack of moe_decode_stack,
+ * with its layer list fixed once, as a command sequence encoded once is
+ * replayed per token on the M5 Max news page, "Effective optimisations"):
+ * validates the shape, n_layers (1..4096), t_max (1..32) and flags, writes
+ * the descriptor table (the n_layers device pointers of layers_host, each
+ * 256-byte aligned) into the workspace with a kernel on `stream`, and fills
+ * *st. ws_bytes >= moe_workspace_bytes(shape, n_layers, t_max). Later calls
+ * that use *st must be ordered after this one (same stream, or synchronised).
+ * moe_decode_layer and moe_decode_stack calls on the same workspace leave the
+ * table intact.
+ */
+int32_t moe_stack_init(moe_stack_t* st, const moe_shape_t* shape, const void* const* layers_host, int32_t n_layers,
+                       int32_t t_max, int32_t flags, void* ws_dev, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * One decode step of an initialised stack on T <= st->t_max rows: the same
+ * computation and results as moe_decode_stack over the stack's layers (ids,
+ * w, h_trace as there, sized by st->n_layers), with the layer pointers read
+ * from the descriptor table in the workspace.
+ */
+int32_t moe_stack_decode(const moe_stack_t* st, int32_t T, const uint16_t* h_in_dev, uint16_t* h_out_dev,
+                         int32_t* ids_dev, float* w_dev, uint16_t* h_trace_dev, moe_stream_t stream);
+
+/*
+ * Reads the status word the last stack call (moe_decode_stack or
+ * moe_stack_decode) on this workspace left, into *status_host (waits for the
+ * stream first): 0 = every cross-workgroup wait was met; 1 = a wait timed out
+ * (about a second without progress, e.g. when other work kept part of the
+ * stack kernel's workgroups off the device), the call's outputs are then
+ * invalid. The word is cleared once per stack call, so a time-out in any of
+ * the call's launches is reported. T must be the T of that call.
  */
 int32_t moe_stack_status(const moe_shape_t* shape, int32_t T, const void* ws_dev, uint32_t* status_host,
                          moe_stream_t stream);
@@ -207,7 +297,8 @@ int32_t moe_stack_status(const moe_shape_t* shape, int32_t T, const void* ws_dev
  * thread's next call into the library. */
 const char* moe_last_error(void);
 
-/* Library version string. */
+/* Library version string; ends in " debug-sync" when MOE_DEBUG_SYNC=1 was
+ * seen at the first call. */
 const char* moe_version(void);
 
 #ifdef __cplusplus

@@ -11,24 +11,34 @@ from ._lib import (  # noqa: F401
     MOE_ERR_ALIGNMENT,
     MOE_ERR_HIP,
     MOE_ERR_INVALID_ARG,
+    MOE_ERR_TIMEOUT,
     MOE_ERR_UNSUPPORTED,
     MOE_ERR_WORKSPACE,
     MOE_OK,
+    MOE_PATH_DEFAULT,
+    MOE_PATH_NO_MFMA,
+    MOE_PATH_PER_LAYER,
     MoeError,
     header_functions,
     lib,
     make_shape,
     moe_decode_layer,
     moe_decode_stack,
+    moe_expert_bytes,
     moe_generate_layer,
     moe_generate_rows,
     moe_last_error,
+    moe_layer_bytes,
     moe_layer_layout,
     moe_matrix_bytes,
     moe_pack_matrix,
     moe_shape_t,
+    moe_stack_decode,
+    moe_stack_init,
     moe_stack_status,
+    moe_stack_t,
     moe_unpack_matrix,
+    moe_validate,
     moe_validate_shape,
     moe_version,
     moe_workspace_bytes,

@@ -27,6 +27,11 @@ MOE_ERR_UNSUPPORTED = -2
 MOE_ERR_ALIGNMENT = -3
 MOE_ERR_WORKSPACE = -4
 MOE_ERR_HIP = -5
+MOE_ERR_TIMEOUT = -6
+
+MOE_PATH_DEFAULT = 0
+MOE_PATH_PER_LAYER = 1
+MOE_PATH_NO_MFMA = 2
 
 c_i32, c_i64, c_u64, c_f32, c_vp, c_sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float,
                                          ctypes.c_void_p, ctypes.c_size_t)
@@ -58,7 +63,30 @@ class moe_layer_layout_t(ctypes.Structure):
                                       "expert_stride", "expert_up", "expert_down", "total_bytes")]
 
 
+class moe_stack_t(ctypes.Structure):
+    _fields_ = [
+        ("shape", moe_shape_t),
+        ("n_layers", c_i32),
+        ("t_max", c_i32),
+        ("flags", c_i32),
+        ("magic", ctypes.c_uint32),
+        ("ws_dev", c_vp),
+        ("ws_bytes", c_sz),
+        ("table_offset", c_i64),
+        ("reserved", c_i64 * 4),
+    ]
+
+
 _lib: Optional[ctypes.CDLL] = None
+
+
+def use_library(path: str) -> None:
+    """Selects another build of the library (e.g. the phase-trace build
+    libmoe_trace.so) before its first use in this process."""
+    global LIB_PATH
+    if _lib is not None and os.path.abspath(path) != os.path.abspath(LIB_PATH):
+        raise RuntimeError("the library is already loaded")
+    LIB_PATH = path
 
 
 def lib() -> ctypes.CDLL:
@@ -76,7 +104,13 @@ def lib() -> ctypes.CDLL:
         L.moe_validate_shape.restype = c_i32
         L.moe_layer_layout.argtypes = [sp, ctypes.POINTER(moe_layer_layout_t)]
         L.moe_layer_layout.restype = c_i32
-        L.moe_workspace_bytes.argtypes = [sp, c_i32]
+        L.moe_validate.argtypes = [sp, c_i32]
+        L.moe_validate.restype = c_i32
+        L.moe_expert_bytes.argtypes = [sp]
+        L.moe_expert_bytes.restype = c_i64
+        L.moe_layer_bytes.argtypes = [sp]
+        L.moe_layer_bytes.restype = c_i64
+        L.moe_workspace_bytes.argtypes = [sp, c_i32, c_i32]
         L.moe_workspace_bytes.restype = c_i64
         L.moe_pack_matrix.argtypes = [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]
         L.moe_pack_matrix.restype = c_i32
@@ -91,6 +125,11 @@ def lib() -> ctypes.CDLL:
         L.moe_decode_stack.argtypes = [sp, ctypes.POINTER(c_vp), c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                        c_sz, c_vp]
         L.moe_decode_stack.restype = c_i32
+        stp = ctypes.POINTER(moe_stack_t)
+        L.moe_stack_init.argtypes = [stp, sp, ctypes.POINTER(c_vp), c_i32, c_i32, c_i32, c_vp, c_sz, c_vp]
+        L.moe_stack_init.restype = c_i32
+        L.moe_stack_decode.argtypes = [stp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]
+        L.moe_stack_decode.restype = c_i32
         L.moe_stack_status.argtypes = [sp, c_i32, c_vp, ctypes.POINTER(ctypes.c_uint32), c_vp]
         L.moe_stack_status.restype = c_i32
         L.moe_last_error.argtypes = []
@@ -140,8 +179,20 @@ def moe_layer_layout(shape: moe_shape_t) -> Dict[str, int]:
     return {n: getattr(out, n) for n, _ in moe_layer_layout_t._fields_}
 
 
-def moe_workspace_bytes(shape: moe_shape_t, T: int) -> int:
-    return _check(lib().moe_workspace_bytes(ctypes.byref(shape), T))
+def moe_validate(shape: moe_shape_t, T: int) -> int:
+    return _check(lib().moe_validate(ctypes.byref(shape), T))
+
+
+def moe_expert_bytes(shape: moe_shape_t) -> int:
+    return _check(lib().moe_expert_bytes(ctypes.byref(shape)))
+
+
+def moe_layer_bytes(shape: moe_shape_t) -> int:
+    return _check(lib().moe_layer_bytes(ctypes.byref(shape)))
+
+
+def moe_workspace_bytes(shape: moe_shape_t, n_layers: int, T: int) -> int:
+    return _check(lib().moe_workspace_bytes(ctypes.byref(shape), n_layers, T))
 
 
 def moe_pack_matrix(bits: int, codes: np.ndarray, scale_bits: np.ndarray, bias_bits: np.ndarray) -> np.ndarray:
@@ -190,6 +241,21 @@ def moe_decode_stack(shape: moe_shape_t, layers_dev: Sequence[int], T: int, h_in
     arr = (c_vp * len(layers_dev))(*[_p(p) for p in layers_dev])
     _check(lib().moe_decode_stack(ctypes.byref(shape), arr, len(layers_dev), T, _p(h_in_dev), _p(h_out_dev),
                                   _p(ids_dev), _p(w_dev), _p(h_trace_dev), _p(ws_dev), ws_bytes, _p(stream)))
+
+
+def moe_stack_init(shape: moe_shape_t, layers_dev: Sequence[int], t_max: int, flags: int, ws_dev: int,
+                   ws_bytes: int, stream: int = 0) -> moe_stack_t:
+    st = moe_stack_t()
+    arr = (c_vp * len(layers_dev))(*[_p(p) for p in layers_dev])
+    _check(lib().moe_stack_init(ctypes.byref(st), ctypes.byref(shape), arr, len(layers_dev), t_max, flags, _p(ws_dev),
+                                ws_bytes, _p(stream)))
+    return st
+
+
+def moe_stack_decode(st: moe_stack_t, T: int, h_in_dev: int, h_out_dev: int, ids_dev: Optional[int],
+                     w_dev: Optional[int], h_trace_dev: Optional[int], stream: int = 0) -> None:
+    _check(lib().moe_stack_decode(ctypes.byref(st), T, _p(h_in_dev), _p(h_out_dev), _p(ids_dev), _p(w_dev),
+                                  _p(h_trace_dev), _p(stream)))
 
 
 def moe_stack_status(shape: moe_shape_t, T: int, ws_dev: int, stream: int = 0) -> int:

@@ -21,6 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
+TRACE_LIB = os.path.join(PKG, "libmoe_trace.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -44,30 +45,36 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, phase_trace: bool = False) -> str:
+    """Builds libmoe.so; phase_trace=True builds libmoe_trace.so instead, whose
+    streaming stack kernel also writes per-phase timestamps into the workspace
+    (compiled with MOE_PHASE_TRACE; a measurement build, never the product)."""
+    bdir = BUILD + ("_trace" if phase_trace else "")
+    lib = TRACE_LIB if phase_trace else LIB
+    defs = ["-DMOE_PHASE_TRACE=1"] if phase_trace else []
+    os.makedirs(bdir, exist_ok=True)
     jobs = []
     objs = []
     for src in HOST_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
+        obj = os.path.join(bdir, src + ".o")
         objs.append(obj)
-        jobs.append(["g++", "-O2", "-fPIC", "-std=c++17", "-Wall", "-I", INCLUDE, "-I", CSRC, "-c",
+        jobs.append(["g++", "-O2", "-fPIC", "-std=c++17", "-Wall", *defs, "-I", INCLUDE, "-I", CSRC, "-c",
                      os.path.join(CSRC, src), "-o", obj])
     for src in HIP_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
+        obj = os.path.join(bdir, src + ".o")
         objs.append(obj)
-        jobs.append([HIPCC, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([HIPCC, *HIP_FLAGS, *defs, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         outs = list(ex.map(_run, jobs))
     if verbose:
         for o in outs:
             if o.strip():
                 print(o)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, phase_trace="--phase-trace" in sys.argv))

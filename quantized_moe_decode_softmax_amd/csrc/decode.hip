@@ -73,7 +73,22 @@ struct Ptrs {
   uint16_t* a_hi;
   uint16_t* a_lo;
   float* ysh;  // shared expert's down projection [T][H] from the matrix-core path, or nullptr
+  // the layer block is table[li] (descriptor table in device memory) when
+  // table is set, else `layer`
+  const uint8_t* const* table;
+  int li;
 };
+
+// up to 64 layer pointers passed by value to the table writer
+struct LayerBatch {
+  static constexpr int kN = 64;
+  const uint8_t* p[kN];
+};
+
+__device__ __forceinline__ Ptrs with_layer(Ptrs p) {
+  if (p.table) p.layer = p.table[p.li];
+  return p;
+}
 
 __device__ __forceinline__ float silu_mul(float g, float v) { return g / (1.0f + expf(-g)) * v; }
 
@@ -293,7 +308,8 @@ __device__ __forceinline__ void swiglu_task(const Dims& d, const Ptrs& p, const 
 // wave loads the task's weight rows and takes token rows wave, wave + nw, ...
 // (a row's arithmetic does not depend on which wave computes it)
 template <int CPL>
-__global__ void __launch_bounds__(256) route_kernel(Dims d, Ptrs p, int n_rt) {
+__global__ void __launch_bounds__(256) route_kernel(Dims d, Ptrs p_, int n_rt) {
+  const Ptrs p = with_layer(p_);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6, task = blockIdx.x;
   const int lpr = lanes_per_row(d.H), rpw = 64 / lpr, sr = lane / lpr, li = lane % lpr;
   if (task < n_rt) {
@@ -418,7 +434,8 @@ __global__ void __launch_bounds__(1024) select_kernel(Dims d, Ptrs p) {
 
 // ---------------------------------------------------------- expert kernel
 template <int CPL>
-__global__ void __launch_bounds__(256, 2) expert_kernel(Dims d, Ptrs p, int tasks_per_unit) {
+__global__ void __launch_bounds__(256, 2) expert_kernel(Dims d, Ptrs p_, int tasks_per_unit) {
+  const Ptrs p = with_layer(p_);
   __shared__ int s_ids[kMaxT * kMaxTopK];
   __shared__ float s_r[kMaxT];
   __shared__ int s_units[kMaxUnits];
@@ -450,7 +467,8 @@ __global__ void __launch_bounds__(256, 2) expert_kernel(Dims d, Ptrs p, int task
 
 // grid: waves of tpw consecutive (row, slot, block) tasks, tps blocks per slot
 template <int CPL>
-__global__ void __launch_bounds__(256, 2) expert_rows_kernel(Dims d, Ptrs p, int tps, int tpw) {
+__global__ void __launch_bounds__(256, 2) expert_rows_kernel(Dims d, Ptrs p_, int tps, int tpw) {
+  const Ptrs p = with_layer(p_);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lpr = lanes_per_row(d.H), rpw = 64 / lpr, sr = lane / lpr, li = lane % lpr;
   constexpr int RP = ExpertPairs<CPL>::RP;
@@ -558,14 +576,16 @@ __device__ __forceinline__ void down_body(const Dims& d, const Ptrs& p, int J) {
 
 // up to 16 waves (one per unit in flight), RD * CPL <= 4
 template <int CPL, int RD>
-__global__ void __launch_bounds__(1024) down_kernel(Dims d, Ptrs p, int J) {
+__global__ void __launch_bounds__(1024) down_kernel(Dims d, Ptrs p_, int J) {
+  const Ptrs p = with_layer(p_);
   down_body<CPL, RD>(d, p, J);
 }
 // up to 12 waves (three per SIMD, as its registers allow) with 8 rows per
 // lane group (J = 16 at K <= 1024): for many token rows, where each unit's
 // activations are read once per workgroup and a wider slice halves those reads
 template <int CPL, int RD>
-__global__ void __launch_bounds__(768) down_kernel_wide(Dims d, Ptrs p, int J) {
+__global__ void __launch_bounds__(768) down_kernel_wide(Dims d, Ptrs p_, int J) {
+  const Ptrs p = with_layer(p_);
   down_body<CPL, RD>(d, p, J);
 }
 
@@ -588,21 +608,13 @@ struct LayerPlan {
   int m_nt, m_ng_route, m_ng_down, m_rt, m_pt, m_down;
 };
 
-// MOE_MFMA=0 keeps every call on the vector-unit kernels (for comparison).
-bool mfma_enabled() {
-  static const bool on = [] {
-    const char* v = getenv("MOE_MFMA");
-    return !(v && v[0] == '0');
-  }();
-  return on;
-}
-
 int mfma_groups_per_load(int groups) {
   const int gpw = (groups + kMfmaWaves - 1) / kMfmaWaves;
   return gpw >= 8 ? 8 : gpw >= 4 ? 4 : 2;
 }
 
-LayerPlan make_plan(const moe_shape_t& s, const moe_layer_layout_t& L, int T) {
+// flags: MOE_PATH_NO_MFMA keeps batches on the vector-unit kernels
+LayerPlan make_plan(const moe_shape_t& s, const moe_layer_layout_t& L, int T, int flags) {
   LayerPlan P;
   Dims& d = P.d;
   d.H = s.hidden;
@@ -666,7 +678,7 @@ LayerPlan make_plan(const moe_shape_t& s, const moe_layer_layout_t& L, int T) {
   int nw = max_units + 1;
   if (nw > (P.d_wide ? 12 : 16)) nw = P.d_wide ? 12 : 16;
   P.d_threads = 64 * nw;
-  P.mfma = T >= kMfmaMinT && s.router_bits == 8 && s.shared_bits == 8 && mfma_enabled();
+  P.mfma = T >= kMfmaMinT && s.router_bits == 8 && s.shared_bits == 8 && !(flags & MOE_PATH_NO_MFMA);
   P.m_nt = T > 16 ? 2 : 1;
   // groups in flight per wave, bounded by registers: 8 only with one token tile
   P.m_ng_route = mfma_groups_per_load(s.hidden / kGroup);
@@ -721,10 +733,14 @@ void launch_down(const LayerPlan& P, const Ptrs& p, hipStream_t st) {
     default: { constexpr int C = 4; __VA_ARGS__; } break; \
   }
 
-int32_t launch_layer(const LayerPlan& P, const WsMap& m, uint8_t* ws, const uint8_t* layer, const uint16_t* h_in,
-                     uint16_t* h_out, int32_t* ids_out, float* w_out, hipStream_t st) {
+// The layer block is `layer`, or entry li of the device table when table is set.
+int32_t launch_layer(const LayerPlan& P, const WsMap& m, uint8_t* ws, const uint8_t* layer,
+                     const uint8_t* const* table, int li, const uint16_t* h_in, uint16_t* h_out, int32_t* ids_out,
+                     float* w_out, hipStream_t st) {
   Ptrs p;
   p.layer = layer;
+  p.table = table;
+  p.li = li;
   p.h_in = h_in;
   p.h_out = h_out;
   p.ids_out = ids_out;
@@ -781,6 +797,85 @@ int32_t check_call(const moe_shape_t* shape, int32_t T, const void* h_in, const 
   return MOE_OK;
 }
 
+// After the launches of an entry point: with MOE_DEBUG_SYNC=1, wait for the
+// stream and report a HIP error (and, for stack calls, a timed-out wait).
+int32_t finish(hipStream_t st, const uint32_t* status_dev) {
+  if (!debug_sync()) return MOE_OK;
+  hipError_t e = hipStreamSynchronize(st);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return set_error(MOE_ERR_HIP, "MOE_DEBUG_SYNC: %s", hipGetErrorString(e));
+  if (status_dev) {
+    uint32_t v = 0;
+    e = hipMemcpy(&v, status_dev, 4, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return set_error(MOE_ERR_HIP, "MOE_DEBUG_SYNC status read: %s", hipGetErrorString(e));
+    if (v) return set_error(MOE_ERR_TIMEOUT, "a cross-workgroup wait of the stack kernel timed out");
+  }
+  return MOE_OK;
+}
+
+__global__ void write_table_kernel(const uint8_t** table, LayerBatch b, int n) {
+  if ((int)threadIdx.x < n) table[threadIdx.x] = b.p[threadIdx.x];
+}
+
+// A stack call: layer blocks from `src`, T rows, workspace map m (of this T).
+int32_t run_stack(const moe_shape_t& s, const LayerSrc& src, int n_layers, int T, int flags, const uint16_t* h_in,
+                  uint16_t* h_out, int32_t* ids, float* w, uint16_t* h_trace, uint8_t* ws, const WsMap& m,
+                  hipStream_t st) {
+  moe_layer_layout_t L;
+  layout_of(s, &L);
+  const LayerPlan P = make_plan(s, L, T, flags);
+  const int64_t th = (int64_t)T * s.hidden;
+  const int64_t tk = (int64_t)T * s.top_k;
+  uint16_t* hb = (uint16_t*)(ws + m.hbuf);
+  if (h_trace) {
+    hipError_t e = hipMemcpyAsync(h_trace, h_in, th * 2, hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) return set_error(MOE_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
+  }
+  // One-row calls run as one streaming kernel per up to 64 layers when the
+  // shape allows it and the device holds its workgroups at once; every other
+  // call runs layer by layer (measured on MI355X, the per-layer kernels beat
+  // a persistent kernel for T >= 2: one select kernel routes all rows, the
+  // routed experts go row by row, the route kernel spreads token rows over
+  // waves). Both give the same results bit for bit.
+  if (!(flags & MOE_PATH_PER_LAYER)) {
+    int32_t rc = launch_stack_t1(s, L, m, ws, src, n_layers, T, h_in, h_out, ids, w, h_trace, st);
+    if (rc != MOE_ERR_UNSUPPORTED) return rc ? rc : finish(st, (const uint32_t*)(ws + m.status));
+    clear_error();
+  }
+  clear_status_kernel<<<1, 64, 0, st>>>((uint32_t*)(ws + m.status));
+  const uint16_t* cur = h_in;
+  for (int l = 0; l < n_layers; ++l) {
+    uint16_t* nxt;
+    if (h_trace) nxt = h_trace + (l + 1) * th;
+    else if (l == n_layers - 1) nxt = h_out;
+    else nxt = hb + (l & 1) * th;
+    int32_t rc = launch_layer(P, m, ws, (const uint8_t*)src.at(l), src.table, l, cur, nxt, ids ? ids + l * tk : nullptr,
+                              w ? w + l * tk : nullptr, st);
+    if (rc) return rc;
+    cur = nxt;
+  }
+  if (h_trace) {
+    hipError_t e = hipMemcpyAsync(h_out, cur, th * 2, hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) return set_error(MOE_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
+  }
+  return finish(st, (const uint32_t*)(ws + m.status));
+}
+
+int32_t check_outputs(const int32_t* ids, const float* w, const uint16_t* h_trace) {
+  if (((uintptr_t)ids % 4) || ((uintptr_t)w % 4) || ((uintptr_t)h_trace % 16))
+    return set_error(MOE_ERR_ALIGNMENT, "ids/w must be 4-byte and h_trace 16-byte aligned");
+  return MOE_OK;
+}
+
+int32_t check_layer_list(const void* const* layers, int n_layers) {
+  if (!layers || n_layers < 1 || n_layers > kMaxLayers) return set_error(MOE_ERR_INVALID_ARG, "bad layer list");
+  for (int l = 0; l < n_layers; ++l) {
+    if (!layers[l]) return set_error(MOE_ERR_INVALID_ARG, "layer %d pointer is NULL", l);
+    if ((uintptr_t)layers[l] % kAlign) return set_error(MOE_ERR_ALIGNMENT, "layer %d not 256-byte aligned", l);
+  }
+  return MOE_OK;
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -798,9 +893,24 @@ extern "C" int32_t moe_decode_layer(const moe_shape_t* shape, const void* layer_
   if (((uintptr_t)ids_dev % 4) || ((uintptr_t)w_dev % 4)) return set_error(MOE_ERR_ALIGNMENT, "ids/w must be 4-byte aligned");
   moe_layer_layout_t L;
   layout_of(*shape, &L);
-  const LayerPlan P = make_plan(*shape, L, T);
-  return launch_layer(P, m, (uint8_t*)ws_dev, (const uint8_t*)layer_dev, h_in_dev, h_out_dev, ids_dev, w_dev,
-                      (hipStream_t)stream);
+  const LayerPlan P = make_plan(*shape, L, T, MOE_PATH_DEFAULT);
+  hipStream_t st = (hipStream_t)stream;
+  rc = launch_layer(P, m, (uint8_t*)ws_dev, (const uint8_t*)layer_dev, nullptr, 0, h_in_dev, h_out_dev, ids_dev, w_dev,
+                    st);
+  return rc ? rc : finish(st, nullptr);
+}
+
+int32_t moe::decode_stack_ws(const moe_shape_t* shape, const void* const* layers_host, int32_t n_layers, int32_t T,
+                             const uint16_t* h_in_dev, uint16_t* h_out_dev, int32_t* ids_dev, float* w_dev,
+                             uint16_t* h_trace_dev, void* ws_dev, size_t ws_bytes, moe_stream_t stream) {
+  WsMap m;
+  int32_t rc = check_call(shape, T, h_in_dev, h_out_dev, ws_dev, ws_bytes, &m);
+  if (rc) return rc;
+  if ((rc = check_layer_list(layers_host, n_layers))) return rc;
+  if ((rc = check_outputs(ids_dev, w_dev, h_trace_dev))) return rc;
+  LayerSrc src{layers_host, nullptr};
+  return run_stack(*shape, src, n_layers, T, MOE_PATH_DEFAULT, h_in_dev, h_out_dev, ids_dev, w_dev, h_trace_dev,
+                   (uint8_t*)ws_dev, m, (hipStream_t)stream);
 }
 
 extern "C" int32_t moe_decode_stack(const moe_shape_t* shape, const void* const* layers_host, int32_t n_layers,
@@ -808,61 +918,60 @@ extern "C" int32_t moe_decode_stack(const moe_shape_t* shape, const void* const*
                                     float* w_dev, uint16_t* h_trace_dev, void* ws_dev, size_t ws_bytes,
                                     moe_stream_t stream) {
   clear_error();
-  WsMap m;
-  int32_t rc = check_call(shape, T, h_in_dev, h_out_dev, ws_dev, ws_bytes, &m);
+  return decode_stack_ws(shape, layers_host, n_layers, T, h_in_dev, h_out_dev, ids_dev, w_dev, h_trace_dev, ws_dev,
+                         ws_bytes, stream);
+}
+
+extern "C" int32_t moe_stack_init(moe_stack_t* st, const moe_shape_t* shape, const void* const* layers_host,
+                                  int32_t n_layers, int32_t t_max, int32_t flags, void* ws_dev, size_t ws_bytes,
+                                  moe_stream_t stream) {
+  clear_error();
+  if (!st) return set_error(MOE_ERR_INVALID_ARG, "stack state is NULL");
+  int32_t rc = check_shape(shape);
   if (rc) return rc;
-  if (!layers_host || n_layers < 1 || n_layers > 4096) return set_error(MOE_ERR_INVALID_ARG, "bad layer list");
-  for (int l = 0; l < n_layers; ++l) {
-    if (!layers_host[l]) return set_error(MOE_ERR_INVALID_ARG, "layer %d pointer is NULL", l);
-    if ((uintptr_t)layers_host[l] % kAlign) return set_error(MOE_ERR_ALIGNMENT, "layer %d not 256-byte aligned", l);
+  if (t_max < 1 || t_max > kMaxT) return set_error(MOE_ERR_INVALID_ARG, "t_max %d not in [1, %d]", t_max, kMaxT);
+  if ((rc = check_layer_list(layers_host, n_layers))) return rc;
+  if (flags & ~(MOE_PATH_PER_LAYER | MOE_PATH_NO_MFMA)) return set_error(MOE_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (!ws_dev) return set_error(MOE_ERR_INVALID_ARG, "workspace is NULL");
+  if ((uintptr_t)ws_dev % kAlign) return set_error(MOE_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+  const int64_t table_off = ws_map(*shape, t_max).total;
+  const int64_t need = table_off + table_bytes(n_layers);
+  if ((int64_t)ws_bytes < need)
+    return set_error(MOE_ERR_WORKSPACE, "workspace %zu bytes < %lld needed", ws_bytes, (long long)need);
+  hipStream_t s = (hipStream_t)stream;
+  const uint8_t** table = (const uint8_t**)((uint8_t*)ws_dev + table_off);
+  for (int l0 = 0; l0 < n_layers; l0 += LayerBatch::kN) {
+    LayerBatch b;
+    const int n = n_layers - l0 < LayerBatch::kN ? n_layers - l0 : LayerBatch::kN;
+    for (int i = 0; i < n; ++i) b.p[i] = (const uint8_t*)layers_host[l0 + i];
+    write_table_kernel<<<1, LayerBatch::kN, 0, s>>>(table + l0, b, n);
   }
-  if (((uintptr_t)ids_dev % 4) || ((uintptr_t)w_dev % 4) || ((uintptr_t)h_trace_dev % 16))
-    return set_error(MOE_ERR_ALIGNMENT, "ids/w must be 4-byte and h_trace 16-byte aligned");
-  hipStream_t st = (hipStream_t)stream;
-  moe_layer_layout_t L;
-  layout_of(*shape, &L);
-  const LayerPlan P = make_plan(*shape, L, T);
-  const int64_t th = (int64_t)T * shape->hidden;
-  const int64_t tk = (int64_t)T * shape->top_k;
-  uint16_t* hb = (uint16_t*)((uint8_t*)ws_dev + m.hbuf);
-  if (h_trace_dev) {
-    hipError_t e = hipMemcpyAsync(h_trace_dev, h_in_dev, th * 2, hipMemcpyDeviceToDevice, st);
-    if (e != hipSuccess) return set_error(MOE_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
-  }
-  // One-row calls run as one streaming kernel per up to 64 layers when the
-  // shape allows it; every other call runs layer by layer (measured on
-  // MI355X, the per-layer kernels now beat a persistent kernel for T >= 2:
-  // one select kernel routes all rows, the routed experts go row by row, the
-  // route kernel spreads token rows over waves). MOE_STACK_KERNEL=0 runs
-  // one-row calls layer by layer too, for comparison; both give the same
-  // results bit for bit.
-  static const bool streaming = [] {
-    const char* v = getenv("MOE_STACK_KERNEL");
-    return !(v && v[0] == '0');
-  }();
-  if (streaming) {
-    rc = launch_stack_t1(*shape, L, m, (uint8_t*)ws_dev, layers_host, n_layers, T, h_in_dev, h_out_dev, ids_dev,
-                         w_dev, h_trace_dev, st);
-    if (rc != MOE_ERR_UNSUPPORTED) return rc;
-    clear_error();
-  }
-  clear_status_kernel<<<1, 64, 0, st>>>((uint32_t*)((uint8_t*)ws_dev + m.status));
-  const uint16_t* cur = h_in_dev;
-  for (int l = 0; l < n_layers; ++l) {
-    uint16_t* nxt;
-    if (h_trace_dev) nxt = h_trace_dev + (l + 1) * th;
-    else if (l == n_layers - 1) nxt = h_out_dev;
-    else nxt = hb + (l & 1) * th;
-    rc = launch_layer(P, m, (uint8_t*)ws_dev, (const uint8_t*)layers_host[l], cur, nxt,
-                      ids_dev ? ids_dev + l * tk : nullptr, w_dev ? w_dev + l * tk : nullptr, st);
-    if (rc) return rc;
-    cur = nxt;
-  }
-  if (h_trace_dev) {
-    hipError_t e = hipMemcpyAsync(h_out_dev, cur, th * 2, hipMemcpyDeviceToDevice, st);
-    if (e != hipSuccess) return set_error(MOE_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
-  }
-  return MOE_OK;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(MOE_ERR_HIP, "descriptor table write failed: %s", hipGetErrorString(e));
+  st->shape = *shape;
+  st->n_layers = n_layers;
+  st->t_max = t_max;
+  st->flags = flags;
+  st->magic = kStackMagic;
+  st->ws_dev = ws_dev;
+  st->ws_bytes = ws_bytes;
+  st->table_offset = table_off;
+  for (int i = 0; i < 4; ++i) st->reserved[i] = 0;
+  return finish(s, nullptr);
+}
+
+extern "C" int32_t moe_stack_decode(const moe_stack_t* st, int32_t T, const uint16_t* h_in_dev, uint16_t* h_out_dev,
+                                    int32_t* ids_dev, float* w_dev, uint16_t* h_trace_dev, moe_stream_t stream) {
+  clear_error();
+  if (!st || st->magic != kStackMagic) return set_error(MOE_ERR_INVALID_ARG, "stack state not initialised by moe_stack_init");
+  if (T < 1 || T > st->t_max) return set_error(MOE_ERR_INVALID_ARG, "T %d not in [1, t_max %d]", T, st->t_max);
+  WsMap m;
+  int32_t rc = check_call(&st->shape, T, h_in_dev, h_out_dev, st->ws_dev, st->ws_bytes, &m);
+  if (rc) return rc;
+  if ((rc = check_outputs(ids_dev, w_dev, h_trace_dev))) return rc;
+  LayerSrc src{nullptr, (const uint8_t* const*)((const uint8_t*)st->ws_dev + st->table_offset)};
+  return run_stack(st->shape, src, st->n_layers, T, st->flags, h_in_dev, h_out_dev, ids_dev, w_dev, h_trace_dev,
+                   (uint8_t*)st->ws_dev, m, (hipStream_t)stream);
 }
 
 extern "C" int32_t moe_stack_status(const moe_shape_t* shape, int32_t T, const void* ws_dev, uint32_t* status_host,

@@ -22,6 +22,8 @@ constexpr int kMaxTopK = 16;
 constexpr int kMaxExperts = 512;
 constexpr int kMaxDim = 8192;
 constexpr int kMaxLayersPerLaunch = 64;
+constexpr int kMaxLayers = 4096;
+constexpr uint32_t kStackMagic = 0x4D4F4553u;  // marks a moe_stack_t filled by moe_stack_init
 constexpr int64_t kAlign = 256;
 // copies of each exchange buffer of the streaming stack kernel (one per XCD)
 constexpr int kExchangeCopies = 8;
@@ -67,14 +69,30 @@ struct WsMap {
   int64_t xh_cs, xl_cs, xa_cs;
   int64_t status;       // u32 [64]           word 0: nonzero after a timed-out wait
   int64_t x_end;        // end of the region the streaming kernel clears per call
+  // per-phase timestamps of the streaming kernel, u64 [64 layers][512 workgroups][16]
+  // (phase-trace builds only; -1 otherwise)
+  int64_t phase_ts;
   int64_t total;
 };
 
 WsMap ws_map(const moe_shape_t& s, int T);
+// Byte range [begin, end) of the workspace that the streaming stack kernel's
+// clear kernel zeroes before a launch: every exchange word, and the status
+// word only before the first launch of a call.
+MOE_HD inline void clear_range(const WsMap& m, bool first_launch, int64_t* begin, int64_t* end) {
+  *begin = m.x_h;
+  *end = first_launch ? m.x_end : m.status;
+}
+// bytes of the descriptor table of n layer pointers (placed after the map of
+// the stack's largest T)
+MOE_HD constexpr inline int64_t table_bytes(int n) { return align_up((int64_t)n * 8, kAlign); }
 
 // thread-local error reporting
 int32_t set_error(int32_t code, const char* fmt, ...);
 void clear_error();
+// MOE_DEBUG_SYNC=1 in the environment (read once): launching entry points
+// wait for their stream and report HIP errors and wait time-outs
+bool debug_sync();
 
 int32_t check_shape(const moe_shape_t* s);
 
@@ -82,8 +100,35 @@ void layout_of(const moe_shape_t& s, moe_layer_layout_t* out);
 
 // One-row stack decode with the streaming kernel (stack1.hip).
 // MOE_ERR_UNSUPPORTED, with nothing launched, for calls it does not handle.
+// Where a stack call finds its layer blocks: a host array of device pointers
+// (moe_decode_stack) or the descriptor table in the workspace (moe_stack_init).
+struct LayerSrc {
+  const void* const* host;         // or nullptr
+  const uint8_t* const* table;     // device, or nullptr
+  const void* at(int l) const { return host ? host[l] : nullptr; }
+};
+
+// One-row stack decode with the streaming kernel (stack1.hip).
+// MOE_ERR_UNSUPPORTED, with nothing launched, for calls it does not handle
+// (also when the device cannot hold all of its workgroups at once).
 int32_t launch_stack_t1(const moe_shape_t& s, const moe_layer_layout_t& L, const WsMap& m, uint8_t* ws,
-                        const void* const* layers, int n_layers, int T, const uint16_t* h_in, uint16_t* h_out,
+                        const LayerSrc& layers, int n_layers, int T, const uint16_t* h_in, uint16_t* h_out,
                         int32_t* ids_out, float* w_out, uint16_t* h_trace_out, moe_stream_t st);
 
+// moe_decode_stack after clear_error(): validation, then the launches, on the
+// given workspace (also the static scratch of the allocation-free variant).
+int32_t decode_stack_ws(const moe_shape_t* shape, const void* const* layers_host, int32_t n_layers, int32_t T,
+                        const uint16_t* h_in_dev, uint16_t* h_out_dev, int32_t* ids_dev, float* w_dev,
+                        uint16_t* h_trace_dev, void* ws_dev, size_t ws_bytes, moe_stream_t stream);
+
 }  // namespace moe
+
+#ifdef MOE_PHASE_TRACE
+// Phase-trace builds only: byte offset of the timestamp region in a workspace
+// for T rows (layout [layer of the last launch][workgroup][16] u64).
+extern "C" int64_t moe_phase_trace_offset(const moe_shape_t* shape, int32_t T);
+#endif
+
+// Host-only test hook (not part of the ABI): out = {clear begin, clear end,
+// status offset, map total} for the shape, T and launch position.
+extern "C" int32_t moe_internal_clear_range(const moe_shape_t* shape, int32_t T, int32_t first_launch, int64_t* out);

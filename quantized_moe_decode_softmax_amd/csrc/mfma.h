@@ -185,7 +185,8 @@ __device__ __forceinline__ void mfma_reduce(MfmaLds& L, float (&v)[NV]) {
 // pairs each (gate rows as columns 0..7, up rows as 8..15). The first pair
 // workgroup also writes r_t and the shared gate sigmoid(r_t gvec . h_t).
 template <int NT, int NG>
-__global__ void __launch_bounds__(kMfmaThreads) route_mfma_kernel(Dims d, Ptrs p, int n_rt) {
+__global__ void __launch_bounds__(kMfmaThreads) route_mfma_kernel(Dims d, Ptrs p_, int n_rt) {
+  const Ptrs p = with_layer(p_);
   __shared__ MfmaLds L;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tl = lane & 15;
   const int G = d.H >> 6;
@@ -278,7 +279,8 @@ __global__ void __launch_bounds__(kMfmaThreads) route_mfma_kernel(Dims d, Ptrs p
 // gate) for 16 output rows per workgroup; a_s = hi + lo from the activation
 // slot k.
 template <int NT, int NG>
-__global__ void __launch_bounds__(kMfmaThreads) down_mfma_kernel(Dims d, Ptrs p) {
+__global__ void __launch_bounds__(kMfmaThreads) down_mfma_kernel(Dims d, Ptrs p_) {
+  const Ptrs p = with_layer(p_);
   __shared__ MfmaLds L;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tl = lane & 15;
   const int G = d.Is >> 6;

@@ -3,6 +3,7 @@
 // call is made here, so every function in this file works without a GPU.
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "internal.h"
@@ -20,6 +21,14 @@ int32_t set_error(int32_t code, const char* fmt, ...) {
 }
 
 void clear_error() { g_err[0] = 0; }
+
+bool debug_sync() {
+  static const bool on = [] {
+    const char* v = getenv("MOE_DEBUG_SYNC");
+    return v != nullptr && v[0] == '1';
+  }();
+  return on;
+}
 
 static bool dim_ok(int v) { return v >= kGroup && v <= kMaxDim && v % kGroup == 0; }
 
@@ -96,6 +105,11 @@ WsMap ws_map(const moe_shape_t& s, int T) {
   m.x_flag = take(m.n_copy * 512 * 8);
   m.status = take(64 * 4);
   m.x_end = off;
+#ifdef MOE_PHASE_TRACE
+  m.phase_ts = take((int64_t)kMaxLayersPerLaunch * 512 * 16 * 8);
+#else
+  m.phase_ts = -1;
+#endif
   m.total = off;
   return m;
 }
@@ -171,12 +185,40 @@ int32_t moe_layer_layout(const moe_shape_t* shape, moe_layer_layout_t* out) {
   return MOE_OK;
 }
 
-int64_t moe_workspace_bytes(const moe_shape_t* shape, int32_t T) {
+int32_t moe_validate(const moe_shape_t* shape, int32_t T) {
   clear_error();
   int32_t rc = check_shape(shape);
   if (rc) return rc;
   if (T < 1 || T > kMaxT) return set_error(MOE_ERR_INVALID_ARG, "T %d not in [1, %d]", T, kMaxT);
-  return ws_map(*shape, T).total;
+  return MOE_OK;
+}
+
+int64_t moe_expert_bytes(const moe_shape_t* shape) {
+  clear_error();
+  int32_t rc = check_shape(shape);
+  if (rc) return rc;
+  moe_layer_layout_t L;
+  layout_of(*shape, &L);
+  return L.expert_stride;
+}
+
+int64_t moe_layer_bytes(const moe_shape_t* shape) {
+  clear_error();
+  int32_t rc = check_shape(shape);
+  if (rc) return rc;
+  moe_layer_layout_t L;
+  layout_of(*shape, &L);
+  return L.total_bytes;
+}
+
+int64_t moe_workspace_bytes(const moe_shape_t* shape, int32_t n_layers, int32_t T) {
+  clear_error();
+  int32_t rc = check_shape(shape);
+  if (rc) return rc;
+  if (T < 1 || T > kMaxT) return set_error(MOE_ERR_INVALID_ARG, "T %d not in [1, %d]", T, kMaxT);
+  if (n_layers < 0 || n_layers > kMaxLayers)
+    return set_error(MOE_ERR_INVALID_ARG, "n_layers %d not in [0, %d]", n_layers, kMaxLayers);
+  return ws_map(*shape, T).total + table_bytes(n_layers);
 }
 
 int32_t moe_pack_matrix(int32_t bits, int32_t rows, int32_t cols, const uint8_t* codes, const uint16_t* scale,
@@ -227,8 +269,32 @@ int32_t moe_unpack_matrix(int32_t bits, int32_t rows, int32_t cols, const void* 
   return MOE_OK;
 }
 
+int32_t moe_internal_clear_range(const moe_shape_t* shape, int32_t T, int32_t first_launch, int64_t* out) {
+  clear_error();
+  int32_t rc = check_shape(shape);
+  if (rc) return rc;
+  if (T < 1 || T > kMaxT || !out) return set_error(MOE_ERR_INVALID_ARG, "bad T or out");
+  const WsMap m = ws_map(*shape, T);
+  clear_range(m, first_launch != 0, &out[0], &out[1]);
+  out[2] = m.status;
+  out[3] = m.total;
+  return MOE_OK;
+}
+
+#ifdef MOE_PHASE_TRACE
+int64_t moe_phase_trace_offset(const moe_shape_t* shape, int32_t T) {
+  clear_error();
+  int32_t rc = check_shape(shape);
+  if (rc) return rc;
+  if (T < 1 || T > kMaxT) return set_error(MOE_ERR_INVALID_ARG, "T %d not in [1, %d]", T, kMaxT);
+  return ws_map(*shape, T).phase_ts;
+}
+#endif
+
 const char* moe_last_error(void) { return g_err; }
 
-const char* moe_version(void) { return "moe-decode-gfx950 0.1"; }
+const char* moe_version(void) {
+  return debug_sync() ? "moe-decode-gfx950 0.2 debug-sync" : "moe-decode-gfx950 0.2";
+}
 
 }  // extern "C"

@@ -72,6 +72,7 @@
 // residual + gate) and "Deferred GPU Expert Compute" (the combined output
 // feeds the next layer on the GPU).
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 
 #include "gemv.h"
@@ -87,6 +88,13 @@ constexpr uint32_t kSpinLimit = 1u << 21;
 constexpr int kMaxWG = 512;
 constexpr int kMaxH = 4096;
 constexpr int kMaxAWords = 12288;  // (k + 1) * imax
+// Slots of the per-phase timestamps of a phase-trace build (wave recording it):
+//  0 layer start (w0)            1 h staged in LDS (w0)        2 phase A computed (w0)
+//  3 all logits seen (w0)        4 top-k done (w0)             5 routed loads issued (w0)
+//  6 routed pairs computed (w0)  7 routed pairs computed (w7)  8 activations published (w0)
+//  9 first down slot's inputs in LDS (w0, after the ready flags)
+// 10 down rows done (w0)        11 combine done (thread 0)   12 shared down inputs fetched (w7)
+constexpr int kPhases = 16;
 
 struct Args {
   int H, E, I, Is, k, imax;
@@ -109,6 +117,11 @@ struct Args {
   int64_t h_cs, l_cs, a_cs;
   int n_copy;
   uint32_t* status;
+  // the launch's layer blocks: table[l0 + l] (a descriptor table in device
+  // memory) when table is set, else layers[l]
+  const uint8_t* const* table;
+  int l0;
+  uint64_t* phase_ts;  // per-phase timestamps [layer][workgroup][kPhases] (phase-trace builds), or null
   const uint8_t* layers[kMaxLayersPerLaunch];
 };
 
@@ -434,12 +447,29 @@ struct Shared {
   // (S.r of the same layer is in place before the first of them)
   uint32_t rank_tag[kMaxTopK];
   uint32_t logit_ep;  // epoch of the layer whose logits wave 0 has seen (so all phase A output exists)
+  uint64_t layers[kMaxLayersPerLaunch];  // the launch's layer blocks
+#ifdef MOE_PHASE_TRACE
+  uint64_t ts[kPhases];  // this layer's phase timestamps (s_memrealtime, 100 MHz)
+#endif
   __attribute__((aligned(16))) uint8_t ring[kWaves][kRingBytes];
   __attribute__((aligned(16))) uint8_t sd[kRingBytes];  // the shared expert's down rows of the slice
 };
 
 // ------------------------------------------------------------- the kernel
 __shared__ Shared S;
+
+// Phase timestamps (builds with MOE_PHASE_TRACE only): lane 0 of the calling
+// wave stores the 100 MHz real-time counter in slot P of the layer's record.
+#ifdef MOE_PHASE_TRACE
+#define MOE_TS(P)                                                           \
+  do {                                                                      \
+    if ((threadIdx.x & 63) == 0) S.ts[P] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#else
+#define MOE_TS(P) \
+  do {            \
+  } while (0)
+#endif
 
 // Per-thread constants of the current layer (values only: the kernel
 // arguments are always referenced directly, never stored).
@@ -841,6 +871,7 @@ __device__ __forceinline__ void route(const Args& a, const Ctx& c, const uint32_
   for (int m = 0; m < M; ++m) want |= (c.lane + 64 * m < c.E ? 1u : 0u) << m;
   poll<M>(a.x_logit + c.cp * c.l_cs + c.lane, [](int m) { return (int64_t)64 * m; }, want, c.ep, rv, a.status);
   lds_st(&S.logit_ep, c.ep);
+  MOE_TS(3);
   int key[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) key[m] = c.lane + 64 * m < c.E ? fkey(r * __uint_as_float(rv[m])) : INT_MIN;
@@ -850,6 +881,7 @@ __device__ __forceinline__ void route(const Args& a, const Ctx& c, const uint32_
   topk_select<M, KF>(key, c.k, my_id, my_w, [ep](int i, int id) {
     if ((threadIdx.x & 63) == 0) lds_st(&S.rank_tag[i], ep << 16 | (uint32_t)id);
   });
+  MOE_TS(4);
   if (c.lane < c.k) {
     S.ids[c.lane] = my_id;
     S.w[c.lane] = my_w;
@@ -862,6 +894,7 @@ __device__ __forceinline__ void route(const Args& a, const Ctx& c, const uint32_
 __device__ __forceinline__ void publish_a(const Args& a, const Ctx& c) {
   lds_barrier();
   if (c.wave == 0 && c.lane == 0) st_copies(a.x_flag + blockIdx.x, 512, c.n_copy, 1u, c.ep);
+  if (c.wave == 0) MOE_TS(8);
 }
 
 // ---- the activation vector of one slot into S.a (one wave): for a routed
@@ -990,10 +1023,13 @@ __device__ __forceinline__ void phases_bc(const Args& a, const Ctx& c) {
         t1 = b_task<CPL_H, CPL_I>(a, c, c.wave + kWaves, id_of);
         pair_load<B, CPL_H>(c, t1, P1);
       }
+      if (c.wave == 0) MOE_TS(5);
       XLane<B, CPL_H> x;
       h_lane<B, CPL_H>(S.h, c.H, c.li_h, c.lpr_h, x);
       if (mb > 0) pair_rows_reg<CPL_H, CPL_I, B>(a, c, t0, P0, x, S.r);
       if (mb > 1) pair_rows_reg<CPL_H, CPL_I, B>(a, c, t1, P1, x, S.r);
+      if (c.wave == 0) MOE_TS(6);
+      if (c.wave == kWaves - 1) MOE_TS(7);
     });
     mb = 0;
   }
@@ -1042,6 +1078,7 @@ __device__ __forceinline__ void phases_bc(const Args& a, const Ctx& c) {
       const Task t = task(j);
       if (t.kind == kDown && t.slot != fetched) {
         fetch_a<NV>(a, c, t.slot);
+        if (c.wave == 0 && fetched < 0) MOE_TS(9);
         fetched = t.slot;
       }
       const uint8_t* buf = S.ring[c.wave] + h * kHalf + off;
@@ -1184,10 +1221,22 @@ __global__ void __launch_bounds__(kThreads) stack1_kernel(Args a) {
   c.li_h = c.lane % c.lpr_h;
   c.sr_h = c.lane / c.lpr_h;
   c.cp = blockIdx.x % c.n_copy;
-  if (threadIdx.x == 0) S.route_ep = S.logit_ep = 0u;  // ordered before their readers by the first barrier below
+  if (threadIdx.x == 0) S.route_ep = S.logit_ep = 0u;  // ordered before their readers by the barrier below
   if (threadIdx.x < kMaxTopK) S.rank_tag[threadIdx.x] = 0u;
+  if ((int)threadIdx.x < a.n_layers)
+    S.layers[threadIdx.x] = (uint64_t)(a.table ? a.table[a.l0 + threadIdx.x] : a.layers[threadIdx.x]);
+  lds_barrier();
   for (int l = 0; l < a.n_layers; ++l) {
-    c.layer = a.layers[l];
+#ifdef MOE_PHASE_TRACE
+    if (threadIdx.x < kPhases) S.ts[threadIdx.x] = 0u;  // phases a path does not pass stay 0
+#endif
+    if (c.wave == 0) MOE_TS(0);
+    {
+      const uint64_t lp = S.layers[l];
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)lp);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(lp >> 32));
+      c.layer = (const uint8_t*)(((uint64_t)hi << 32) | lo);
+    }
     c.ep = (uint32_t)l + 1;
     // phase A weights stream in while h_l is polled
     int na;
@@ -1208,8 +1257,10 @@ __global__ void __launch_bounds__(kThreads) stack1_kernel(Args a) {
     }
     stage_h(a, c, l);
     lds_barrier();
+    if (c.wave == 0) MOE_TS(1);
     phase_a_compute<CPL_H, CPL_I, RB, SB>(a, c);
     if (c.wave == 0) {
+      MOE_TS(2);
     if constexpr (ME != 0) {
       MOE_T1_RBITS(RB, c.rbits, B, route<CPL_H, B, ME, SH::k>(a, c, gvn));
     } else {
@@ -1224,6 +1275,7 @@ __global__ void __launch_bounds__(kThreads) stack1_kernel(Args a) {
       lds_st(&S.route_ep, c.ep);
     } else if (c.wave == kWaves - 1) {
       shared_down_fetch<SH::NV>(a, c);
+      MOE_TS(12);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // phase A ring reads done
     if (blockIdx.x == 0 && threadIdx.x < c.k) {  // wave 0, whose routing is complete
@@ -1231,9 +1283,16 @@ __global__ void __launch_bounds__(kThreads) stack1_kernel(Args a) {
       if (a.w_out) a.w_out[(int64_t)l * c.k + threadIdx.x] = S.w[threadIdx.x];
     }
     phases_bc<CPL_H, CPL_I, EB, SB, SH::KI, SH::KS, SH::NV>(a, c);
+    if (c.wave == 0) MOE_TS(10);
     lds_barrier();
     combine(a, c, l);
     lds_barrier();
+#ifdef MOE_PHASE_TRACE
+    if (a.phase_ts && threadIdx.x < kPhases) {
+      uint64_t* dst = a.phase_ts + ((int64_t)l * kMaxWG + blockIdx.x) * kPhases;
+      dst[threadIdx.x] = threadIdx.x == 11 ? __builtin_amdgcn_s_memrealtime() : S.ts[threadIdx.x];
+    }
+#endif
   }
 }
 
@@ -1245,8 +1304,38 @@ __global__ void clear_words(uint64_t* p, int64_t n) {
 }  // namespace t1
 
 // ----------------------------------------------------------------- host side
+// Compute units of the current device (cached per device id).
+static int device_cus(int* dev_out) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  *dev_out = dev;
+  int n = dev < kMaxDev ? cache[dev].load(std::memory_order_relaxed) : 0;
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return -1;
+  if (dev < kMaxDev) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Whether the device can hold `nwg` workgroups of kernel `fn` at once (the
+// stack kernel's workgroups wait on each other). Cached per (device, kernel).
+static bool co_resident(const void* fn, int slot, int dev, int n_cu, int nwg) {
+  constexpr int kMaxDev = 64, kSlots = 8;
+  static std::atomic<int> cache[kMaxDev][kSlots];  // blocks per CU + 1, 0 = unknown
+  int per_cu = -1;
+  if (dev < kMaxDev && slot < kSlots) per_cu = cache[dev][slot].load(std::memory_order_relaxed) - 1;
+  if (per_cu < 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, t1::kThreads, 0) != hipSuccess) return false;
+    per_cu = nb;
+    if (dev < kMaxDev && slot < kSlots) cache[dev][slot].store(nb + 1, std::memory_order_relaxed);
+  }
+  return (int64_t)per_cu * n_cu >= nwg;
+}
+
 int32_t launch_stack_t1(const moe_shape_t& s, const moe_layer_layout_t& L, const WsMap& m, uint8_t* ws,
-                        const void* const* layers, int n_layers, int T, const uint16_t* h_in, uint16_t* h_out,
+                        const LayerSrc& layers, int n_layers, int T, const uint16_t* h_in, uint16_t* h_out,
                         int32_t* ids_out, float* w_out, uint16_t* h_trace_out, moe_stream_t stream) {
   using namespace t1;
   if (T != 1) return MOE_ERR_UNSUPPORTED;
@@ -1259,13 +1348,9 @@ int32_t launch_stack_t1(const moe_shape_t& s, const moe_layer_layout_t& L, const
   if ((int64_t)(s.top_k + 1) * imax > kMaxAWords) return MOE_ERR_UNSUPPORTED;
   const int cpl_h = chunks_per_lane(s.hidden), cpl_i = chunks_per_lane(imax);
   if (cpl_h > 2 || cpl_i > 2) return MOE_ERR_UNSUPPORTED;
-  static int n_cu = 0;
-  if (n_cu == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
-      return set_error(MOE_ERR_HIP, "cannot query the compute unit count");
-  }
+  int dev = 0;
+  const int n_cu = device_cus(&dev);
+  if (n_cu <= 0) return set_error(MOE_ERR_HIP, "cannot query the compute unit count");
   int J = (s.hidden + n_cu - 1) / n_cu;
   J = J < 2 ? 2 : (J + 1) & ~1;
   if (J > 16) return MOE_ERR_UNSUPPORTED;
@@ -1327,10 +1412,13 @@ int32_t launch_stack_t1(const moe_shape_t& s, const moe_layer_layout_t& L, const
   a.a_cs = m.xa_cs;
   a.n_copy = m.n_copy;
   a.status = (uint32_t*)(ws + m.status);
+  a.phase_ts = m.phase_ts >= 0 ? (uint64_t*)(ws + m.phase_ts) : nullptr;
   // the kernel instance: one specialised for the whole shape (35B-A3B and
   // 397B-A17B layers, the tiny bf16-router layer) when every value matches,
   // else a generic one
   void (*launch)(const Args&, hipStream_t) = nullptr;
+  const void* fn = nullptr;
+  int slot = 0;
   auto matches = [&](auto shape) {
     using SH = decltype(shape);
     return SH::H == a.H && SH::E == a.E && SH::I == a.I && SH::Is == a.Is && SH::k == a.k && SH::RB == a.rbits &&
@@ -1345,21 +1433,35 @@ int32_t launch_stack_t1(const moe_shape_t& s, const moe_layer_layout_t& L, const
   using A3B = FixedShape<2048, 256, 512, 512, 8, 8, 6, 8, 256>;
   using A17B = FixedShape<4096, 512, 1024, 1024, 10, 8, 4, 4, 256>;
   using Tiny = FixedShape<256, 16, 128, 128, 2, 16, 4, 4, 256>;
+  using R11 = RtShape<1, 1>;
+  using R21 = RtShape<2, 1>;
+  using R12 = RtShape<1, 2>;
+  using R22 = RtShape<2, 2>;
+#define MOE_T1_PICK(SHAPE, SLOT)                                                                           \
+  do {                                                                                                    \
+    launch = [](const Args& x, hipStream_t q) { stack1_kernel<SHAPE><<<x.nwg, kThreads, 0, q>>>(x); };   \
+    fn = (const void*)stack1_kernel<SHAPE>;                                                               \
+    slot = SLOT;                                                                                          \
+  } while (0)
   if (matches(A3B())) {
-    launch = [](const Args& x, hipStream_t q) { stack1_kernel<A3B><<<x.nwg, kThreads, 0, q>>>(x); };
+    MOE_T1_PICK(A3B, 0);
   } else if (matches(A17B())) {
-    launch = [](const Args& x, hipStream_t q) { stack1_kernel<A17B><<<x.nwg, kThreads, 0, q>>>(x); };
+    MOE_T1_PICK(A17B, 1);
   } else if (matches(Tiny())) {
-    launch = [](const Args& x, hipStream_t q) { stack1_kernel<Tiny><<<x.nwg, kThreads, 0, q>>>(x); };
+    MOE_T1_PICK(Tiny, 2);
   } else if (cpl_h == 1 && cpl_i == 1) {
-    launch = [](const Args& x, hipStream_t q) { stack1_kernel<RtShape<1, 1>><<<x.nwg, kThreads, 0, q>>>(x); };
+    MOE_T1_PICK(R11, 3);
   } else if (cpl_h == 2 && cpl_i == 1) {
-    launch = [](const Args& x, hipStream_t q) { stack1_kernel<RtShape<2, 1>><<<x.nwg, kThreads, 0, q>>>(x); };
+    MOE_T1_PICK(R21, 4);
   } else if (cpl_h == 1) {
-    launch = [](const Args& x, hipStream_t q) { stack1_kernel<RtShape<1, 2>><<<x.nwg, kThreads, 0, q>>>(x); };
+    MOE_T1_PICK(R12, 5);
   } else {
-    launch = [](const Args& x, hipStream_t q) { stack1_kernel<RtShape<2, 2>><<<x.nwg, kThreads, 0, q>>>(x); };
+    MOE_T1_PICK(R22, 6);
   }
+#undef MOE_T1_PICK
+  // every workgroup must be resident at once: otherwise the caller runs the
+  // stack layer by layer
+  if (!co_resident(fn, slot, dev, n_cu, nwg)) return MOE_ERR_UNSUPPORTED;
   hipStream_t st = (hipStream_t)stream;
   const int64_t H = s.hidden, k = s.top_k;
   uint16_t* hb = (uint16_t*)(ws + m.hbuf);
@@ -1368,15 +1470,20 @@ int32_t launch_stack_t1(const moe_shape_t& s, const moe_layer_layout_t& L, const
     const int nl = n_layers - l0 < kMaxLayersPerLaunch ? n_layers - l0 : kMaxLayersPerLaunch;
     const bool last = l0 + nl == n_layers;
     a.n_layers = nl;
-    for (int l = 0; l < nl; ++l) a.layers[l] = (const uint8_t*)layers[l0 + l];
+    a.table = layers.table;
+    a.l0 = l0;
+    for (int l = 0; l < nl; ++l) a.layers[l] = (const uint8_t*)layers.at(l0 + l);
     a.h_in = cur;
     a.h_out = last ? h_out : hb + ((l0 / kMaxLayersPerLaunch) & 1) * H;
     a.ids_out = ids_out ? ids_out + (int64_t)l0 * k : nullptr;
     a.w_out = w_out ? w_out + (int64_t)l0 * k : nullptr;
     a.h_trace = h_trace_out ? h_trace_out + (int64_t)(l0 + 1) * H : nullptr;
-    // zero the exchange words and the status word (no stale epoch can match)
-    const int64_t nclr = (m.x_end - m.x_h) / 8;
-    clear_words<<<64, 256, 0, st>>>((uint64_t*)(ws + m.x_h), nclr);
+    // zero the exchange words (no stale epoch can match), and the status
+    // word only before the first launch: a time-out in any launch of the
+    // call stays reported (and makes the later launches' waits give up at once)
+    int64_t cb, ce;
+    clear_range(m, l0 == 0, &cb, &ce);
+    clear_words<<<64, 256, 0, st>>>((uint64_t*)(ws + cb), (ce - cb) / 8);
     launch(a, st);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return set_error(MOE_ERR_HIP, "stack kernel launch failed: %s", hipGetErrorString(e));

@@ -2,13 +2,14 @@
 
 ``DeviceStack`` owns one HBM buffer per layer (filled by the library's seeded
 generator, or by the caller with packed weights), a workspace, and calls
-``moe_decode_layer`` / ``moe_decode_stack`` on the current torch stream. No
-step of the method runs here.
+``moe_decode_layer``, ``moe_stack_init`` / ``moe_stack_decode`` (the whole
+stack) and ``moe_decode_stack`` (any list of its layers) on the current torch
+stream. No step of the method runs here.
 """
 
 from __future__ import annotations
 
-from typing import List, Optional, Sequence
+from typing import Dict, List, Optional, Sequence
 
 import torch
 
@@ -34,13 +35,21 @@ class DeviceStack:
         self.layers: List[torch.Tensor] = [
             torch.empty(self.layout["total_bytes"], dtype=torch.uint8, device=device) for _ in range(n_layers)
         ]
-        self.ws_bytes = L.moe_workspace_bytes(self.shape, t_max)
+        self.ws_bytes = L.moe_workspace_bytes(self.shape, n_layers, t_max)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
         # read the stack kernel's status word after every stack call (waits for the stream)
         self.check_status = False
         if seed is not None:
             for i, buf in enumerate(self.layers):
                 L.moe_generate_layer(self.shape, seed, i, buf.data_ptr(), _stream())
+        self._states: Dict[int, L.moe_stack_t] = {}
+
+    def state(self, flags: int = L.MOE_PATH_DEFAULT) -> "L.moe_stack_t":
+        """The initialised stack (all layers, descriptor table in the workspace) for a path choice."""
+        if flags not in self._states:
+            self._states[flags] = L.moe_stack_init(self.shape, [b.data_ptr() for b in self.layers], self.t_max,
+                                                   flags, self.ws.data_ptr(), self.ws_bytes, _stream())
+        return self._states[flags]
 
     @classmethod
     def from_workload(cls, w: Workload, n_layers: Optional[int] = None, t_max: Optional[int] = None, seed: int = 0):
@@ -61,8 +70,10 @@ class DeviceStack:
         return out, ids, w
 
     def stack(self, h: torch.Tensor, n_layers: Optional[int] = None, trace: bool = False, routing: bool = True,
-              out: Optional[torch.Tensor] = None, layer_ids: Optional[Sequence[int]] = None):
-        """Runs layers[0:n_layers] (or the listed layer indices) as one moe_decode_stack call."""
+              out: Optional[torch.Tensor] = None, layer_ids: Optional[Sequence[int]] = None,
+              flags: Optional[int] = None):
+        """Runs the whole stack through moe_stack_decode (the initialised stack for ``flags``), or
+        layers[0:n_layers] / the listed layer indices as one moe_decode_stack call."""
         T = h.shape[0]
         sel = list(layer_ids) if layer_ids is not None else list(range(n_layers or self.n_layers))
         n = len(sel)
@@ -70,9 +81,16 @@ class DeviceStack:
         ids = torch.empty((n, T, self.k), dtype=torch.int32, device=self.device) if routing else None
         w = torch.empty((n, T, self.k), dtype=torch.float32, device=self.device) if routing else None
         tr = torch.empty((n + 1, T, self.H), dtype=torch.bfloat16, device=self.device) if trace else None
-        L.moe_decode_stack(self.shape, [self.layers[i].data_ptr() for i in sel], T, h.data_ptr(), out.data_ptr(),
-                           None if ids is None else ids.data_ptr(), None if w is None else w.data_ptr(),
-                           None if tr is None else tr.data_ptr(), self.ws.data_ptr(), self.ws_bytes, _stream())
+        pi = None if ids is None else ids.data_ptr()
+        pw = None if w is None else w.data_ptr()
+        pt = None if tr is None else tr.data_ptr()
+        if sel == list(range(self.n_layers)) or flags is not None:
+            if sel != list(range(self.n_layers)):
+                raise ValueError("path flags apply to the whole initialised stack")
+            L.moe_stack_decode(self.state(flags or 0), T, h.data_ptr(), out.data_ptr(), pi, pw, pt, _stream())
+        else:
+            L.moe_decode_stack(self.shape, [self.layers[i].data_ptr() for i in sel], T, h.data_ptr(), out.data_ptr(),
+                               pi, pw, pt, self.ws.data_ptr(), self.ws_bytes, _stream())
         if self.check_status:
             st = self.status(T)
             if st != 0:

@@ -6,9 +6,12 @@ projection run as grouped dequant-GEMMs on v_mfma_f32_16x16x32_bf16.
   pass criteria), for one and two token tiles (T = 9, 16, 17, 32), ragged
   router tiles (E not a multiple of 16), one group per wave and several;
 * the 397B-A17B low-bit shape (H 4096, 512 experts, 3-bit routed experts,
-  8-bit shared expert and router) at T = 32: sampled rows against the oracle
-  run on that row alone, the two-layer stack equal to chained layer calls,
-  and bitwise-repeatable results.
+  8-bit shared expert and router; all 15 layers resident) at T = 32: all 32
+  rows of layer 0 and of the deepest layer (14) against the oracle, the
+  two-layer stack equal to chained layer calls, and bitwise-repeatable
+  results;
+* the same batch with the matrix cores switched off (MOE_PATH_NO_MFMA) agrees
+  with the oracle too.
 """
 
 import sys
@@ -22,6 +25,7 @@ from oracle import gen as ogen  # noqa: E402
 from oracle.moe import layer_forward  # noqa: E402
 from quantized_moe_decode_softmax_amd import WORKLOADS  # noqa: E402
 from quantized_moe_decode_softmax_amd.runtime import DeviceStack, bf16_bits  # noqa: E402
+from tests.oracle_pool import oracle_rows  # noqa: E402
 from tests.parity import check_layer, oracle_shape  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -64,15 +68,24 @@ def test_mfma_layer_parity(name, kw):
     torch.cuda.empty_cache()
 
 
-def test_mfma_a17b_lowbit_T32():
+@pytest.fixture(scope="module")
+def lowbit():
     w = WORKLOADS["a17b_lowbit"]
-    ds = DeviceStack(w.shape_kwargs(), n_layers=2, t_max=32)
+    ds = DeviceStack(w.shape_kwargs(), n_layers=w.n_layers, t_max=32)
     ds.check_status = True
+    torch.cuda.synchronize()
+    yield ds
+    del ds
+    torch.cuda.empty_cache()
+
+
+def test_mfma_a17b_lowbit_T32(lowbit):
+    ds = lowbit
     osh = oracle_shape(ds.kw)
     x = ds.rows(1000, 32)
     y, ids, wt = ds.layer(x, 0)
     y2, ids2, wt2 = ds.layer(x, 0)
-    out, sids, swt, tr = ds.stack(x, trace=True)
+    out, sids, swt, tr = ds.stack(x, trace=True, layer_ids=[0, 1])
     h1, i1, w1 = ds.layer(y, 1)
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16)) and torch.equal(ids, ids2) and torch.equal(wt, wt2)
@@ -81,13 +94,41 @@ def test_mfma_a17b_lowbit_T32():
     assert torch.equal(sids[0], ids) and torch.equal(sids[1], i1) and torch.equal(swt[1], w1)
     units = len(np.unique(ids.cpu().numpy()))
     log(f"  [a17b_lowbit T=32] unique experts in layer 0: {units}")
-    yb, ih, wh = bf16_bits(y), ids.cpu().numpy(), wt.cpu().numpy()
     xh = ogen.bf16_bits_to_f64(bf16_bits(x))
-    lw = ogen.GeneratedLayer(osh, 0, 0)
-    for t in (0, 7, 16, 31):
-        ref = layer_forward(lw, xh[t:t + 1])
-        r = check_layer(yb[t:t + 1], ih[t:t + 1], wh[t:t + 1], ref)
-        log(f"  [a17b_lowbit T=32] row {t} vs oracle on that row: {r}")
-        assert r.ok, (t, r)
-    del ds
-    torch.cuda.empty_cache()
+    ref = oracle_rows(osh, 0, [0], xh, chain=False)[0]
+    r = check_layer(bf16_bits(y), ids.cpu().numpy(), wt.cpu().numpy(), ref)
+    log(f"  [a17b_lowbit T=32] layer 0, all 32 rows vs oracle: {r}")
+    assert r.ok, r
+
+
+def test_mfma_a17b_lowbit_deepest_layer(lowbit):
+    ds = lowbit
+    osh = oracle_shape(ds.kw)
+    x = ds.rows(1014, 32)
+    y, ids, wt = ds.layer(x, 14)
+    torch.cuda.synchronize()
+    ref = oracle_rows(osh, 0, [14], ogen.bf16_bits_to_f64(bf16_bits(x)), chain=False)[0]
+    r = check_layer(bf16_bits(y), ids.cpu().numpy(), wt.cpu().numpy(), ref)
+    log(f"  [a17b_lowbit T=32] layer 14, all 32 rows vs oracle: {r}")
+    assert r.ok, r
+
+
+def test_lowbit_vector_path_matches_oracle(lowbit):
+    """MOE_PATH_NO_MFMA keeps the router and shared expert on the vector units:
+    the whole 15-layer stack runs; its layer 0 agrees with the oracle and with
+    the matrix-core path's routing."""
+    from quantized_moe_decode_softmax_amd import MOE_PATH_NO_MFMA
+
+    ds = lowbit
+    osh = oracle_shape(ds.kw)
+    x = ds.rows(1000, 32)
+    out, ids, wt, tr = ds.stack(x, trace=True, flags=MOE_PATH_NO_MFMA)
+    out_m, ids_m, wt_m, tr_m = ds.stack(x, trace=True)
+    torch.cuda.synchronize()
+    assert ds.status(32) == 0
+    ref = oracle_rows(osh, 0, [0], ogen.bf16_bits_to_f64(bf16_bits(x)), chain=False)[0]
+    r = check_layer(bf16_bits(tr[1]), ids[0].cpu().numpy(), wt[0].cpu().numpy(), ref)
+    log(f"  [a17b_lowbit T=32, vector path] layer 0 vs oracle: {r}")
+    assert r.ok, r
+    agree = float((ids[0] == ids_m[0]).float().mean())
+    log(f"  [a17b_lowbit T=32] layer-0 ids equal on both paths: {agree:.3f} of entries")

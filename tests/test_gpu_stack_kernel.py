@@ -13,7 +13,10 @@ dense router among them), at T = 1 and T = 2:
 * the status word reports that every wait was met;
 * layer 0 of the stack agrees with the oracle (same input, pass criteria of
   tests/parity.py);
-* a stack longer than 64 layers (two launches) equals its layer calls.
+* a stack longer than 64 layers (two launches of the streaming kernel at
+  T = 1) equals its layer calls;
+* the initialised stack run with MOE_PATH_PER_LAYER (kernels per layer at
+  T = 1) equals the streaming kernel bit for bit.
 """
 
 import sys
@@ -94,14 +97,22 @@ def test_stack_kernel_full_rows_T32():
     torch.cuda.empty_cache()
 
 
-def test_stack_longer_than_one_launch():
-    """70 layers run as two launches (64 + 6); the boundary hands h over in the workspace."""
+@pytest.mark.parametrize("T", [1, 2])
+def test_stack_longer_than_one_launch(T):
+    """70 layers: at T = 1 two launches of the streaming kernel (64 + 6) whose
+    boundary hands h over in the workspace (with the trace, ids and weights
+    offset by the first launch's layers), at T = 2 kernels per layer; both equal
+    70 chained one-layer calls bit for bit, and every wait was met."""
     kw = shp(256, 16, 128, 2, 128, 16, 4, 4)
     n = 70
     ds = DeviceStack(kw, n, t_max=2, seed=3)
     ds.check_status = True
-    x = ds.rows(9, 2)
+    x = ds.rows(9, T)
     out, ids, w, tr = ds.stack(x, trace=True)
+    out_nt, ids_nt, w_nt, _ = ds.stack(x)  # no trace: the second launch's output goes to h_out directly
+    assert torch.equal(out.view(torch.int16), out_nt.view(torch.int16))
+    assert torch.equal(ids, ids_nt) and torch.equal(w, w_nt)
+    assert ds.status(T) == 0
     h = x
     for l in range(n):
         h, il, wl = ds.layer(h, l)
@@ -110,5 +121,24 @@ def test_stack_longer_than_one_launch():
     assert torch.equal(out.view(torch.int16), h.view(torch.int16))
     ids_h = ids.cpu().numpy()
     assert np.all((ids_h >= 0) & (ids_h < 16))
+    del ds
+    torch.cuda.empty_cache()
+
+
+def test_per_layer_flag_equals_streaming_kernel():
+    """The same one-row stack through the persistent streaming kernel and, with
+    MOE_PATH_PER_LAYER, through the per-layer kernels: bitwise equal."""
+    from quantized_moe_decode_softmax_amd import MOE_PATH_PER_LAYER
+
+    kw = shp(2048, 256, 512, 8, 512, 8, 6, 8)
+    ds = DeviceStack(kw, 4, t_max=1, seed=13)
+    ds.check_status = True
+    for s in range(3):
+        x = ds.rows(700 + s, 1)
+        out, ids, w, tr = ds.stack(x, trace=True)
+        out2, ids2, w2, tr2 = ds.stack(x, trace=True, flags=MOE_PATH_PER_LAYER)
+        torch.cuda.synchronize()
+        assert torch.equal(tr.view(torch.int16), tr2.view(torch.int16)), s
+        assert torch.equal(ids, ids2) and torch.equal(w, w2), s
     del ds
     torch.cuda.empty_cache()

@@ -67,14 +67,67 @@ def test_workload_sizes():
 
 def test_workspace_bytes():
     s = shape_of("a3b")
-    w1 = moe.moe_workspace_bytes(s, 1)
-    w8 = moe.moe_workspace_bytes(s, 8)
+    w1 = moe.moe_workspace_bytes(s, 0, 1)
+    w8 = moe.moe_workspace_bytes(s, 0, 8)
     assert 0 < w1 < w8 < 64 << 20
+    # the descriptor table of an initialised stack: 8 bytes per layer, 256-byte granules
+    assert moe.moe_workspace_bytes(s, 40, 1) == w1 + 512
+    assert moe.moe_workspace_bytes(s, 1, 1) == w1 + 256
+    assert moe.moe_workspace_bytes(s, 4096, 8) == w8 + 4096 * 8
+    for nl, T in [(0, 0), (0, 33), (-1, 1), (4097, 1)]:
+        with pytest.raises(moe.MoeError) as e:
+            moe.moe_workspace_bytes(s, nl, T)
+        assert e.value.code == moe.MOE_ERR_INVALID_ARG
+
+
+def test_validate_and_sizes():
+    s = shape_of("a3b")
+    for T in (1, 8, 32):
+        assert moe.moe_validate(s, T) == 0
+    for T in (0, 33):
+        with pytest.raises(moe.MoeError) as e:
+            moe.moe_validate(s, T)
+        assert e.value.code == moe.MOE_ERR_INVALID_ARG
     with pytest.raises(moe.MoeError) as e:
-        moe.moe_workspace_bytes(s, 0)
-    assert e.value.code == moe.MOE_ERR_INVALID_ARG
-    with pytest.raises(moe.MoeError):
-        moe.moe_workspace_bytes(s, 33)
+        moe.moe_validate(shape_of("a3b", expert_bits=5), 1)
+    assert e.value.code == moe.MOE_ERR_UNSUPPORTED
+    lay = moe.moe_layer_layout(s)
+    assert moe.moe_expert_bytes(s) == lay["expert_stride"] == 2555904
+    assert moe.moe_layer_bytes(s) == lay["total_bytes"]
+    # the flash-moe page's ~6.75 MB expert: 4096 x 1024, 4-bit, read as MiB
+    a17 = shape_of("a17b")
+    assert moe.moe_expert_bytes(a17) == 7077888
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_layer_bytes(shape_of("a3b", group=32))
+    assert e.value.code == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_stack_clear_ranges():
+    """The streaming kernel's per-launch clear covers every exchange word, and the
+    status word only before a call's first launch (a time-out in an earlier
+    launch of the same call stays reported)."""
+    for name in WORKLOADS:
+        s = shape_of(name)
+        for T in (1, 8):
+            b0, e0, st_off, total = moe_internal_clear_range(s, T, True)
+            b1, e1, st1, _ = moe_internal_clear_range(s, T, False)
+            assert (b0, st_off) == (b1, st1)
+            assert b0 < st_off < e0 <= total  # first launch: exchange words and status
+            assert e1 == st_off               # later launches: everything before the status word
+            assert b0 % 256 == 0 and e1 % 256 == 0 and e0 % 256 == 0
+            assert total == moe.moe_workspace_bytes(s, 0, T)
+
+
+def moe_internal_clear_range(s, T, first):
+    import ctypes
+
+    L = moe.lib()
+    f = L.moe_internal_clear_range
+    f.argtypes = [ctypes.POINTER(moe.moe_shape_t), ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]
+    f.restype = ctypes.c_int32
+    out = (ctypes.c_int64 * 4)()
+    assert f(ctypes.byref(s), T, 1 if first else 0, out) == 0
+    return tuple(out)
 
 
 @pytest.mark.parametrize(
@@ -114,7 +167,7 @@ def test_top_k_above_experts_rejected():
 def test_decode_argument_errors_return_before_launch():
     """Every one of these fails in host validation; no device pointer is touched."""
     s = shape_of("tiny")
-    ws = moe.moe_workspace_bytes(s, 2)
+    ws = moe.moe_workspace_bytes(s, 0, 2)
     A = 1 << 20  # 256-aligned fake addresses, never dereferenced
     cases = [
         (dict(T=0), moe.MOE_ERR_INVALID_ARG),
@@ -152,6 +205,94 @@ def test_decode_argument_errors_return_before_launch():
     with pytest.raises(moe.MoeError) as e:
         moe.moe_generate_layer(s, 0, 0, A * 16 + 4)
     assert e.value.code == moe.MOE_ERR_ALIGNMENT
+
+
+def test_stack_init_argument_errors_return_before_launch():
+    """moe_stack_init / moe_stack_decode validate on the host before any launch."""
+    s = shape_of("tiny")
+    A = 1 << 20
+    ws = moe.moe_workspace_bytes(s, 2, 4)
+    ok = dict(layers=[A * 16, A * 24], t_max=4, flags=0, ws=A * 32, ws_bytes=ws)
+    cases = [
+        (dict(layers=[]), moe.MOE_ERR_INVALID_ARG),
+        (dict(layers=[A * 16, 0]), moe.MOE_ERR_INVALID_ARG),
+        (dict(layers=[A * 16, A * 16 + 128]), moe.MOE_ERR_ALIGNMENT),
+        (dict(t_max=0), moe.MOE_ERR_INVALID_ARG),
+        (dict(t_max=33), moe.MOE_ERR_INVALID_ARG),
+        (dict(flags=4), moe.MOE_ERR_INVALID_ARG),
+        (dict(ws=0), moe.MOE_ERR_INVALID_ARG),
+        (dict(ws=A * 32 + 16), moe.MOE_ERR_ALIGNMENT),
+        (dict(ws_bytes=ws - 1), moe.MOE_ERR_WORKSPACE),  # the table does not fit
+    ]
+    for over, code in cases:
+        a = dict(ok)
+        a.update(over)
+        with pytest.raises(moe.MoeError) as e:
+            moe.moe_stack_init(s, a["layers"], a["t_max"], a["flags"], a["ws"], a["ws_bytes"])
+        assert e.value.code == code, (over, e.value)
+    # an uninitialised state is refused
+    st = moe.moe_stack_t()
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_stack_decode(st, 1, A * 2, A * 4, None, None, None)
+    assert e.value.code == moe.MOE_ERR_INVALID_ARG
+
+
+def _gpu_visible() -> bool:
+    try:
+        import torch
+
+        return torch.cuda.device_count() > 0
+    except Exception:  # pragma: no cover
+        return False
+
+
+DEBUG_SYNC_PROBE = r"""
+import json, sys
+sys.path.insert(0, sys.argv[1])
+import quantized_moe_decode_softmax_amd as moe
+from quantized_moe_decode_softmax_amd import WORKLOADS
+s = moe.make_shape(**WORKLOADS["tiny"].shape_kwargs())
+A = 1 << 20
+out = {"version": moe.moe_version()}
+def code(f):
+    try:
+        f()
+        return 0
+    except moe.MoeError as e:
+        return e.code
+ws = moe.moe_workspace_bytes(s, 1, 2)
+out["bad_T"] = code(lambda: moe.moe_decode_layer(s, A * 16, 0, A * 2, A * 4, None, None, A * 32, ws))
+out["layer"] = code(lambda: moe.moe_decode_layer(s, A * 16, 2, A * 2, A * 4, None, None, A * 32, ws))
+out["stack"] = code(lambda: moe.moe_decode_stack(s, [A * 16], 1, A * 2, A * 4, None, None, None, A * 32, ws))
+out["init"] = code(lambda: moe.moe_stack_init(s, [A * 16], 2, 0, A * 32, ws))
+out["msg"] = moe.moe_last_error()
+print(json.dumps(out))
+"""
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="launches with placeholder pointers; only meaningful with no GPU")
+@pytest.mark.parametrize("debug", ["0", "1"])
+def test_debug_sync_and_hip_error_mapping_without_device(debug):
+    """MOE_DEBUG_SYNC=1 is read once and reported by moe_version; validation still
+    comes first, and with no device a launching call maps the HIP failure to
+    MOE_ERR_HIP (its launch fails before any synchronisation)."""
+    import json
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, MOE_DEBUG_SYNC=debug)
+    r = subprocess.run([sys.executable, "-c", DEBUG_SYNC_PROBE, root], env=env, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr
+    out = json.loads(r.stdout.strip().splitlines()[-1])
+    assert out["version"].endswith("debug-sync") == (debug == "1")
+    assert out["bad_T"] == moe.MOE_ERR_INVALID_ARG
+    assert out["layer"] == moe.MOE_ERR_HIP
+    assert out["stack"] == moe.MOE_ERR_HIP
+    assert out["init"] == moe.MOE_ERR_HIP
+    assert out["msg"] != ""
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 6, 8])
