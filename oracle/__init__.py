@@ -19,13 +19,20 @@ Modules
     renormalised softmax top-k, SwiGLU experts, sigmoid-gated shared expert,
     weighted combine + residual, and a layer stack that hands bf16 h between
     layers.
+``oracle.dense``
+    Dense group-affine matrix-vector products of the non-expert projections
+    (fused Q/K/V reading one input, attention output, lm_head).
+``oracle.attention``
+    Grouped-query decode attention of verify rows over a bf16 K/V cache.
+``oracle.gdn``
+    One decode step of the Gated DeltaNet recurrence (gated delta rule).
 
 Every floating-point step is fp64; bf16 appears only where the workload fixes
 it (stored weights' scales/biases, bf16 vectors, the bf16 hidden state handed
 between layers).
 """
 
-from . import gen, moe  # noqa: F401
+from . import attention, dense, gdn, gen, moe  # noqa: F401
 from .gen import (  # noqa: F401
     MoEShape,
     GeneratedLayer,

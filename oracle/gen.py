@@ -60,6 +60,10 @@ MASK64 = (1 << 64) - 1
 
 # tensor ids and fields of the draw stream
 T_GATE, T_UP, T_DOWN, T_ROUTER, T_GATEVEC, T_X = 0, 1, 2, 3, 4, 5
+# dense (non-expert) projections of a layer: query, key, value, attention
+# output, lm_head; their sub-seed uses the slot DENSE_SLOT of the layer
+T_Q, T_K, T_V, T_O, T_LM = 6, 7, 8, 9, 10
+DENSE_SLOT = (1 << 20) - 1
 F_CODE, F_SCALE, F_BIAS = 0, 1, 2
 GROUP = 64
 # tag of the x-row sub-seed ("x_rows" in ASCII)
@@ -184,6 +188,12 @@ def gen_qmat(sub: int, tensor: int, rows: int, k: int, bits: int) -> QMat:
     s = gen_scales(sub, tensor, rows, k, bits)
     b = gen_biases(sub, tensor, s, bits)
     return c, s, b
+
+
+def dense_matrix(seed: int, layer: int, tensor: int, rows: int, k: int, bits: int) -> QMat:
+    """A dense projection's packed-as-arrays matrix [rows, k] (codes, scales,
+    biases) from the sub-seed of (layer, DENSE_SLOT) and its tensor id."""
+    return gen_qmat(sub_seed(seed, layer, DENSE_SLOT), tensor, rows, k, bits)
 
 
 class GeneratedLayer:
