@@ -293,6 +293,25 @@ int32_t moe_stack_decode(const moe_stack_t* st, int32_t T, const uint16_t* h_in_
 int32_t moe_stack_status(const moe_shape_t* shape, int32_t T, const void* ws_dev, uint32_t* status_host,
                          moe_stream_t stream);
 
+/*
+ * moe_decode_stack for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, computation and results, but no workspace argument:
+ * the workspace is a static device array inside the library, 4 MiB per GPU,
+ * held from the first call on that GPU until the process ends. The call
+ * allocates nothing (no hipMalloc / hipFree, no allocating library routine).
+ * A shape and T whose workspace (moe_workspace_bytes(shape, 0, T)) exceeds
+ * 4 MiB is rejected with MOE_ERR_WORKSPACE before anything is launched (every
+ * shape of 2048 or 4096 hidden here fits at T = 32). Every call on one GPU
+ * uses that GPU's one array: calls that overlap on one GPU (different
+ * streams, or host threads without ordering) race and give undefined
+ * results; calls ordered on one stream are safe. moe_stack_status does not
+ * read this array.
+ */
+int32_t moe_decode_stack_static(const moe_shape_t* shape, const void* const* layers_host, int32_t n_layers,
+                                int32_t T, const uint16_t* h_in_dev, uint16_t* h_out_dev, int32_t* ids_dev,
+                                float* w_dev, uint16_t* h_trace_dev, moe_stream_t stream);
+
 /* Message for the last failure on this thread ("" if none). Valid until the
  * thread's next call into the library. */
 const char* moe_last_error(void);

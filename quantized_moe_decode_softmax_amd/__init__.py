@@ -24,6 +24,7 @@ from ._lib import (  # noqa: F401
     make_shape,
     moe_decode_layer,
     moe_decode_stack,
+    moe_decode_stack_static,
     moe_expert_bytes,
     moe_generate_layer,
     moe_generate_rows,

@@ -130,6 +130,9 @@ def lib() -> ctypes.CDLL:
         L.moe_stack_init.restype = c_i32
         L.moe_stack_decode.argtypes = [stp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]
         L.moe_stack_decode.restype = c_i32
+        L.moe_decode_stack_static.argtypes = [sp, ctypes.POINTER(c_vp), c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                              c_vp]
+        L.moe_decode_stack_static.restype = c_i32
         L.moe_stack_status.argtypes = [sp, c_i32, c_vp, ctypes.POINTER(ctypes.c_uint32), c_vp]
         L.moe_stack_status.restype = c_i32
         L.moe_last_error.argtypes = []
@@ -241,6 +244,14 @@ def moe_decode_stack(shape: moe_shape_t, layers_dev: Sequence[int], T: int, h_in
     arr = (c_vp * len(layers_dev))(*[_p(p) for p in layers_dev])
     _check(lib().moe_decode_stack(ctypes.byref(shape), arr, len(layers_dev), T, _p(h_in_dev), _p(h_out_dev),
                                   _p(ids_dev), _p(w_dev), _p(h_trace_dev), _p(ws_dev), ws_bytes, _p(stream)))
+
+
+def moe_decode_stack_static(shape: moe_shape_t, layers_dev: Sequence[int], T: int, h_in_dev: int, h_out_dev: int,
+                            ids_dev: Optional[int], w_dev: Optional[int], h_trace_dev: Optional[int],
+                            stream: int = 0) -> None:
+    arr = (c_vp * len(layers_dev))(*[_p(p) for p in layers_dev])
+    _check(lib().moe_decode_stack_static(ctypes.byref(shape), arr, len(layers_dev), T, _p(h_in_dev), _p(h_out_dev),
+                                         _p(ids_dev), _p(w_dev), _p(h_trace_dev), _p(stream)))
 
 
 def moe_stack_init(shape: moe_shape_t, layers_dev: Sequence[int], t_max: int, flags: int, ws_dev: int,
