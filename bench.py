@@ -235,6 +235,224 @@ def phase_trace(w, K: int, W: int) -> int:
     return 0
 
 
+def bench_gemv(K: int, W: int, rows_per_step: int) -> int:
+    """Dense 8-bit projections of the 35B-A3B shape through moe_gemv: per step,
+    for each of the 10 full-attention layers a fused Q/K/V call (4096 + 512 +
+    512 rows x 2048) and an attention output call (2048 x 4096), then one
+    lm_head call (32768 x 2048, the draft vocabulary the PureDrive card names),
+    each layer with its own seeded weights (272 MB per step, beyond the
+    256 MB memory-side cache), T token rows from seeded x."""
+    import torch
+
+    from quantized_moe_decode_softmax_amd import _lib as Lb
+
+    T = rows_per_step
+    H, QD, KD, V, n_att = 2048, 16 * 256, 2 * 256, 32768, 10
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def mat(rows, cols, layer, tensor):
+        b = torch.empty(Lb.moe_matrix_bytes(8, rows, cols), dtype=torch.uint8, device="cuda")
+        Lb.moe_generate_matrix(8, rows, cols, 0, layer, tensor, b.data_ptr(), stream)
+        return b
+
+    layers = [dict(q=mat(QD, H, l, 6), k=mat(KD, H, l, 7), v=mat(KD, H, l, 8), o=mat(H, QD, l, 9))
+              for l in range(n_att)]
+    lm = mat(V, H, 0, 10)
+    x = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    xo = torch.empty((T, QD), dtype=torch.bfloat16, device="cuda")
+    Lb.moe_generate_rows(1000, T, H, x.data_ptr(), stream)
+    Lb.moe_generate_rows(1001, T, QD, xo.data_ptr(), stream)
+    yq = torch.empty((T, QD), dtype=torch.float32, device="cuda")
+    yk = torch.empty((T, KD), dtype=torch.float32, device="cuda")
+    yv = torch.empty((T, KD), dtype=torch.float32, device="cuda")
+    yo = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    yl = torch.empty((T, V), dtype=torch.float32, device="cuda")
+    alg = {"qkv": (QD + 2 * KD) * _matrix_alg_bytes(8, 1, H), "o_proj": _matrix_alg_bytes(8, H, QD),
+           "lm_head": _matrix_alg_bytes(8, V, H)}
+    ev = {k: [] for k in alg}
+
+    def step(timed):
+        for L in layers:
+            e0 = torch.cuda.Event(enable_timing=True) if timed else None
+            e1 = torch.cuda.Event(enable_timing=True) if timed else None
+            e2 = torch.cuda.Event(enable_timing=True) if timed else None
+            if timed:
+                e0.record()
+            Lb.moe_gemv(8, H, T, x.data_ptr(), [(L["q"].data_ptr(), QD, yq.data_ptr()),
+                                                 (L["k"].data_ptr(), KD, yk.data_ptr()),
+                                                 (L["v"].data_ptr(), KD, yv.data_ptr())], stream)
+            if timed:
+                e1.record()
+            Lb.moe_gemv(8, QD, T, xo.data_ptr(), [(L["o"].data_ptr(), H, yo.data_ptr())], stream)
+            if timed:
+                e2.record()
+                ev["qkv"].append((e0, e1))
+                ev["o_proj"].append((e1, e2))
+        e3 = torch.cuda.Event(enable_timing=True) if timed else None
+        e4 = torch.cuda.Event(enable_timing=True) if timed else None
+        if timed:
+            e3.record()
+        Lb.moe_gemv(8, H, T, x.data_ptr(), [(lm.data_ptr(), V, yl.data_ptr())], stream)
+        if timed:
+            e4.record()
+            ev["lm_head"].append((e3, e4))
+
+    for _ in range(W):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) / 1e3 for k, v in ev.items()}
+    step_bytes = n_att * (alg["qkv"] + alg["o_proj"]) + alg["lm_head"]
+    gbps = {k: alg[k] / per[k] / 1e9 for k in alg}
+    res = {
+        "metric": "dense 8-bit projection GEMV GB/s (fused Q/K/V, attention output, lm_head) vs 8 TB/s",
+        "value": round(step_bytes * K / wall / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(wall / K * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": (f"35B-A3B dense projections, T={T}: 10 x (fused QKV 5120x2048 + o-proj 2048x4096) "
+                                f"+ lm_head 32768x2048, 8-bit group 64, seeded weights per layer"),
+                   "T": T, "bytes_per_step": step_bytes},
+        "per_call_us": {k: round(v * 1e6, 2) for k, v in per.items()},
+        "per_call_GBps": {k: round(v, 1) for k, v in gbps.items()},
+        "roofline": {"bound": "hbm", "kernel": "gemv_kernel (lm_head call)", "achieved": round(gbps["lm_head"], 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps["lm_head"] / HBM_PEAK_GBPS, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def bench_attn(K: int, W: int, T: int, ctx: int) -> int:
+    """GQA decode attention of the 35B-A3B shape through moe_gqa_decode: 16
+    query heads, 2 KV heads, head dim 256, bf16 K/V cache of `ctx` positions
+    per layer (about 2 KB per position and layer, the card's ~20 KB per token
+    over 10 attention layers); per step one call for each of the 10 layers
+    (own caches), T verify rows at the end of the context."""
+    import torch
+
+    from quantized_moe_decode_softmax_amd import _lib as Lb
+
+    n_q, n_kv, d, n_att = 16, 2, 256, 10
+    stream = torch.cuda.current_stream().cuda_stream
+    shape = Lb.moe_attn_shape_t(n_q, n_kv, d, ctx)
+    caches = []
+    for l in range(n_att):
+        k = torch.empty((n_kv, ctx, d), dtype=torch.bfloat16, device="cuda")
+        v = torch.empty((n_kv, ctx, d), dtype=torch.bfloat16, device="cuda")
+        Lb.moe_generate_rows(2000 + 2 * l, n_kv * ctx, d, k.data_ptr(), stream)
+        Lb.moe_generate_rows(2001 + 2 * l, n_kv * ctx, d, v.data_ptr(), stream)
+        caches.append((k, v))
+    q = torch.empty((T, n_q, d), dtype=torch.bfloat16, device="cuda")
+    Lb.moe_generate_rows(77, T * n_q, d, q.data_ptr(), stream)
+    o = torch.empty((T, n_q, d), dtype=torch.float32, device="cuda")
+    wsb = Lb.moe_gqa_workspace_bytes(shape, T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    p0 = ctx - T
+    kv_bytes = n_kv * ctx * d * 2 * 2  # K and V of every visible position, read once per call
+    ev = []
+
+    def step(timed):
+        for k, v in caches:
+            if timed:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+            Lb.moe_gqa_decode(shape, T, p0, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), ws.data_ptr(),
+                              wsb, stream)
+            if timed:
+                e1.record()
+                ev.append((e0, e1))
+
+    for _ in range(W):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    res = {
+        "metric": "GQA decode attention: KV-cache GB/s vs 8 TB/s",
+        "value": round(kv_bytes / per / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(wall / K * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": (f"35B-A3B attention shape: 16 q / 2 KV heads, head dim 256, bf16 KV cache of {ctx} "
+                                f"positions per layer, 10 layers, T={T} verify rows"), "T": T, "context": ctx,
+                   "kv_bytes_per_call": kv_bytes},
+        "per_call_us": round(per * 1e6, 2),
+        "roofline": {"bound": "hbm", "kernel": "attn_partial_kernel + attn_combine_kernel (one call)",
+                     "achieved": round(kv_bytes / per / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(kv_bytes / per / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None},
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def bench_gdn(K: int, W: int, T: int) -> int:
+    """Gated DeltaNet decode steps through moe_gdn_step: 30 layers (the card's
+    30 GDN layers of the 35B-A3B model), each with its own fp32 state of 32
+    value heads x 128 x 128 (16 key heads; a reading, the pages give no GDN
+    shape), T tokens per call; the state is read and written once per call."""
+    import torch
+
+    from quantized_moe_decode_softmax_amd import _lib as Lb
+
+    n_k, n_v, dk, dv, n_gdn = 16, 32, 128, 128, 30
+    stream = torch.cuda.current_stream().cuda_stream
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    states = [0.1 * torch.randn((n_v, dv, dk), generator=g, device="cuda") for _ in range(n_gdn)]
+    q = torch.nn.functional.normalize(torch.randn((T, n_k, dk), generator=g, device="cuda"), dim=-1)
+    k = torch.nn.functional.normalize(torch.randn((T, n_k, dk), generator=g, device="cuda"), dim=-1)
+    v = torch.randn((T, n_v, dv), generator=g, device="cuda")
+    al = 0.5 + 0.5 * torch.rand((T, n_v), generator=g, device="cuda")
+    be = torch.rand((T, n_v), generator=g, device="cuda")
+    o = torch.empty((T, n_v, dv), device="cuda")
+    shape = Lb.moe_gdn_shape_t(n_k, n_v, dk, dv)
+    state_bytes = n_v * dv * dk * 4
+    ev = []
+
+    def step(timed):
+        for st in states:
+            if timed:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+            Lb.moe_gdn_step(shape, T, st.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(), al.data_ptr(),
+                            be.data_ptr(), o.data_ptr(), stream)
+            if timed:
+                e1.record()
+                ev.append((e0, e1))
+
+    for _ in range(W):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    traffic = 2 * state_bytes  # read once, written once
+    res = {
+        "metric": "Gated DeltaNet decode step: state GB/s vs 8 TB/s", "value": round(traffic / per / 1e9, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(wall / K * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": (f"30 GDN layers, 16 key / 32 value heads of 128 x 128, fp32 state, T={T}"), "T": T,
+                   "state_bytes_per_call": state_bytes},
+        "per_call_us": round(per * 1e6, 2),
+        "roofline": {"bound": "hbm", "kernel": "gdn_kernel (one call)", "achieved": round(traffic / per / 1e9, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(traffic / per / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,6 +464,13 @@ def main() -> int:
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
     ap.add_argument("--rows", type=int, default=0, help="token rows per step (default: the workload's T)")
     ap.add_argument("--phase-trace", action="store_true", help="per-phase timestamps (phase-trace build)")
+    ap.add_argument("--op", choices=["moe", "gemv", "attn", "gdn"], default="moe",
+                    help="moe: the MoE stack (default); gemv: the dense projections of the 35B-A3B shape; "
+                         "attn: GQA decode attention of the 35B-A3B shape")
+    ap.add_argument("--ctx", type=int, default=131072, help="--op attn: context positions per layer")
+    ap.add_argument("--api", choices=["stack", "pointers"], default="stack",
+                    help="stack: moe_stack_init once + moe_stack_decode per step (layer pointers in the workspace); "
+                         "pointers: moe_decode_stack with the host array of layer pointers per step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding of this "
@@ -253,6 +478,12 @@ def main() -> int:
         return 2
     if args.copy_probe:
         return copy_probe(args.copy_probe)
+    if args.op == "gemv":
+        return bench_gemv(min(args.steps, 200), args.warmup, args.rows or 1)
+    if args.op == "gdn":
+        return bench_gdn(min(args.steps, 200), args.warmup, args.rows or 1)
+    if args.op == "attn":
+        return bench_attn(min(args.steps, 100), args.warmup, args.rows or 1, args.ctx)
     if args.phase_trace:
         from quantized_moe_decode_softmax_amd import WORKLOADS as _W
 
@@ -278,9 +509,14 @@ def main() -> int:
 
     stream = torch.cuda.current_stream().cuda_stream
     st = ds.state()  # moe_stack_init: the descriptor table of the 40 layers in the workspace, once
+    ptrs = [b.data_ptr() for b in ds.layers]
 
     def step(x, idp, wp):
-        Lb.moe_stack_decode(st, T, x.data_ptr(), out.data_ptr(), idp, wp, None, stream)
+        if args.api == "stack":
+            Lb.moe_stack_decode(st, T, x.data_ptr(), out.data_ptr(), idp, wp, None, stream)
+        else:
+            Lb.moe_decode_stack(ds.shape, ptrs, T, x.data_ptr(), out.data_ptr(), idp, wp, None, ds.ws.data_ptr(),
+                                ds.ws_bytes, stream)
 
     for s in range(W):
         step(xs[s], ids[0].data_ptr(), wts[0].data_ptr())

@@ -312,6 +312,112 @@ int32_t moe_decode_stack_static(const moe_shape_t* shape, const void* const* lay
                                 int32_t T, const uint16_t* h_in_dev, uint16_t* h_out_dev, int32_t* ids_dev,
                                 float* w_dev, uint16_t* h_trace_dev, moe_stream_t stream);
 
+/*
+ * Dense projections (the non-expert weights): y_m = W_m x for n_mats
+ * group-affine matrices W_m [rows_m, cols] that share one input x, computed
+ * in one launch that reads x once (the fused Q/K/V projection kernel of the
+ * Qwen3.5-397B on M5 Max news page, "Effective optimisations"); the attention
+ * output projection and lm_head are the one-matrix case (8-bit on the
+ * PureDrive card, "Summary"). W_m[r, c] = code * scale + bias in groups of 64
+ * along c (flash-moe news page, "FMA-optimised dequant kernel").
+ *   bits      : code width of every matrix of the call, {2, 3, 4, 6, 8}
+ *   cols      : K, a multiple of 64 in [64, 8192]
+ *   T         : token rows, 1 <= T <= 32
+ *   x_dev     : bf16 [T, cols], 16-byte aligned
+ *   mats_host : host array of n_mats (1..4) descriptors: w_dev a packed
+ *               matrix block (moe_matrix_bytes layout, 256-byte aligned),
+ *               rows_m in [1, 2^22] (all matrices together at most 2^22),
+ *               y_dev fp32 [T, rows_m] (4-byte aligned, overlapping neither
+ *               x nor another output)
+ * Results are fp32 and not rounded; row t of a T-row call equals a one-row
+ * call on row t bit for bit.
+ */
+typedef struct moe_gemv_mat {
+  const void* w_dev;
+  int32_t rows;
+  int32_t reserved;
+  float* y_dev;
+} moe_gemv_mat_t;
+
+int32_t moe_gemv(int32_t bits, int32_t cols, int32_t T, const uint16_t* x_dev, const moe_gemv_mat_t* mats_host,
+                 int32_t n_mats, moe_stream_t stream);
+
+/*
+ * Synthetic dense projection: writes one packed matrix [rows, cols] with
+ * `bits`-bit codes (moe_matrix_bytes bytes at dst_dev, 256-byte aligned) from
+ * the generator of moe_generate_layer, with the sub-seed of (seed, layer,
+ * slot 2^20 - 1) and the draw stream of `tensor` (query 6, key 7, value 8,
+ * attention output 9, lm_head 10; any id in [6, 1023] is accepted).
+ */
+int32_t moe_generate_matrix(int32_t bits, int32_t rows, int32_t cols, uint64_t seed, int32_t layer, int32_t tensor,
+                            void* dst_dev, moe_stream_t stream);
+
+/*
+ * Grouped-query decode attention of T verify rows over a bf16 K/V cache
+ * (PureDrive card, "How it works": K/V read once for all query heads of a KV
+ * head and all verify rows, split along the keys with split points and
+ * summation order that depend only on the row's position; "Beyond this
+ * checkpoint": 16 query heads, 2 KV heads, head dimension 256). Row i is at
+ * position p0 + i and attends to positions 0 .. p0 + i:
+ *   o[i, h] = sum_j softmax_j(q[i, h] . K[h / g, j] / sqrt(d)) V[h / g, j],
+ * g = n_q / n_kv. The keys are split at fixed multiples of 512 positions, so
+ * row i of a T-row call equals a one-row call with p0 + i bit for bit.
+ *   shape  : n_q, n_kv with n_q a multiple of n_kv, n_q / n_kv <= 16 (<= 8
+ *            at head_dim 256), n_q <= 128; head_dim in {64, 128, 256};
+ *            max_seq (cache length)
+ *            in [1, 2^24]
+ *   T      : 1..8 rows; p0 >= 0 with p0 + T <= max_seq
+ *   q_dev  : bf16 [T, n_q, head_dim]; k_dev, v_dev: bf16 [n_kv, max_seq,
+ *            head_dim] (positions 0 .. p0 + T - 1 filled with finite values;
+ *            the rest is not read); o_dev: fp32 [T, n_q, head_dim]; all
+ *            16-byte aligned
+ *   ws_dev : ws_bytes >= moe_gqa_workspace_bytes(shape, T), 256-byte aligned
+ */
+typedef struct moe_attn_shape {
+  int32_t n_q;
+  int32_t n_kv;
+  int32_t head_dim;
+  int32_t max_seq;
+} moe_attn_shape_t;
+
+int64_t moe_gqa_workspace_bytes(const moe_attn_shape_t* shape, int32_t T);
+
+int32_t moe_gqa_decode(const moe_attn_shape_t* shape, int32_t T, int32_t p0, const uint16_t* q_dev,
+                       const uint16_t* k_dev, const uint16_t* v_dev, float* o_dev, void* ws_dev, size_t ws_bytes,
+                       moe_stream_t stream);
+
+/*
+ * One decode step of the Gated DeltaNet layers' recurrence for T tokens in
+ * order (PureDrive card, "Summary": 30 Gated DeltaNet layers in the 35B-A3B
+ * model; flash-moe news page, "Accelerate BLAS活用": the recurrence as
+ * cblas_sscal / cblas_sgemv / cblas_sger), the gated delta rule of Yang,
+ * Kautz & Hatamizadeh (ICLR 2025): for each value head h with key head
+ * kh = h / (n_v / n_k) and each token t,
+ *   S_h <- alpha[t,h] S_h;  u = S_h k[t,kh];
+ *   S_h <- S_h + beta[t,h] (v[t,h] - u) k[t,kh]^T;  o[t,h] = S_h q[t,kh].
+ * q and k arrive normalised (the projections, convolution and normalisation
+ * before the recurrence are not part of this step). Token t of a T-token call
+ * equals the t-th of T one-token calls in order, bit for bit.
+ *   shape     : d_k in {64, 128, 256}; d_v in [1, 4096]; n_v a multiple of
+ *               n_k, n_v <= 1024
+ *   state_dev : fp32 [n_v, d_v, d_k], read and overwritten with the state
+ *               after the last token (16-byte aligned)
+ *   q_dev, k_dev : fp32 [T, n_k, d_k] (16-byte aligned); v_dev: fp32
+ *               [T, n_v, d_v]; alpha_dev, beta_dev: fp32 [T, n_v]; o_dev:
+ *               fp32 [T, n_v, d_v]; the inputs must not overlap the state or
+ *               o; 1 <= T <= 32
+ */
+typedef struct moe_gdn_shape {
+  int32_t n_k;
+  int32_t n_v;
+  int32_t d_k;
+  int32_t d_v;
+} moe_gdn_shape_t;
+
+int32_t moe_gdn_step(const moe_gdn_shape_t* shape, int32_t T, float* state_dev, const float* q_dev,
+                     const float* k_dev, const float* v_dev, const float* alpha_dev, const float* beta_dev,
+                     float* o_dev, moe_stream_t stream);
+
 /* Message for the last failure on this thread ("" if none). Valid until the
  * thread's next call into the library. */
 const char* moe_last_error(void);

@@ -26,7 +26,15 @@ from ._lib import (  # noqa: F401
     moe_decode_stack,
     moe_decode_stack_static,
     moe_expert_bytes,
+    moe_attn_shape_t,
+    moe_gdn_shape_t,
+    moe_gdn_step,
+    moe_gemv,
+    moe_gemv_mat_t,
     moe_generate_layer,
+    moe_generate_matrix,
+    moe_gqa_decode,
+    moe_gqa_workspace_bytes,
     moe_generate_rows,
     moe_last_error,
     moe_layer_bytes,

@@ -77,6 +77,18 @@ class moe_stack_t(ctypes.Structure):
     ]
 
 
+class moe_gemv_mat_t(ctypes.Structure):
+    _fields_ = [("w_dev", c_vp), ("rows", c_i32), ("reserved", c_i32), ("y_dev", c_vp)]
+
+
+class moe_attn_shape_t(ctypes.Structure):
+    _fields_ = [("n_q", c_i32), ("n_kv", c_i32), ("head_dim", c_i32), ("max_seq", c_i32)]
+
+
+class moe_gdn_shape_t(ctypes.Structure):
+    _fields_ = [("n_k", c_i32), ("n_v", c_i32), ("d_k", c_i32), ("d_v", c_i32)]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -133,6 +145,18 @@ def lib() -> ctypes.CDLL:
         L.moe_decode_stack_static.argtypes = [sp, ctypes.POINTER(c_vp), c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,
                                               c_vp]
         L.moe_decode_stack_static.restype = c_i32
+        L.moe_gemv.argtypes = [c_i32, c_i32, c_i32, c_vp, ctypes.POINTER(moe_gemv_mat_t), c_i32, c_vp]
+        L.moe_gemv.restype = c_i32
+        L.moe_generate_matrix.argtypes = [c_i32, c_i32, c_i32, c_u64, c_i32, c_i32, c_vp, c_vp]
+        L.moe_generate_matrix.restype = c_i32
+        ap = ctypes.POINTER(moe_attn_shape_t)
+        L.moe_gqa_workspace_bytes.argtypes = [ap, c_i32]
+        L.moe_gqa_workspace_bytes.restype = c_i64
+        L.moe_gqa_decode.argtypes = [ap, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]
+        L.moe_gqa_decode.restype = c_i32
+        L.moe_gdn_step.argtypes = [ctypes.POINTER(moe_gdn_shape_t), c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                   c_vp]
+        L.moe_gdn_step.restype = c_i32
         L.moe_stack_status.argtypes = [sp, c_i32, c_vp, ctypes.POINTER(ctypes.c_uint32), c_vp]
         L.moe_stack_status.restype = c_i32
         L.moe_last_error.argtypes = []
@@ -273,6 +297,35 @@ def moe_stack_status(shape: moe_shape_t, T: int, ws_dev: int, stream: int = 0) -
     v = ctypes.c_uint32(0)
     _check(lib().moe_stack_status(ctypes.byref(shape), T, _p(ws_dev), ctypes.byref(v), _p(stream)))
     return v.value
+
+
+def moe_gemv(bits: int, cols: int, T: int, x_dev: int, mats: Sequence, stream: int = 0) -> None:
+    """mats: sequence of (w_dev, rows, y_dev) device addresses / row counts."""
+    arr = (moe_gemv_mat_t * max(1, len(mats)))()
+    for i, (w, r, y) in enumerate(mats):
+        arr[i] = moe_gemv_mat_t(_p(w), r, 0, _p(y))
+    _check(lib().moe_gemv(bits, cols, T, _p(x_dev), arr, len(mats), _p(stream)))
+
+
+def moe_generate_matrix(bits: int, rows: int, cols: int, seed: int, layer: int, tensor: int, dst_dev: int,
+                        stream: int = 0) -> None:
+    _check(lib().moe_generate_matrix(bits, rows, cols, seed, layer, tensor, _p(dst_dev), _p(stream)))
+
+
+def moe_gqa_workspace_bytes(shape: moe_attn_shape_t, T: int) -> int:
+    return _check(lib().moe_gqa_workspace_bytes(ctypes.byref(shape), T))
+
+
+def moe_gqa_decode(shape: moe_attn_shape_t, T: int, p0: int, q_dev: int, k_dev: int, v_dev: int, o_dev: int,
+                   ws_dev: int, ws_bytes: int, stream: int = 0) -> None:
+    _check(lib().moe_gqa_decode(ctypes.byref(shape), T, p0, _p(q_dev), _p(k_dev), _p(v_dev), _p(o_dev), _p(ws_dev),
+                                ws_bytes, _p(stream)))
+
+
+def moe_gdn_step(shape: moe_gdn_shape_t, T: int, state_dev: int, q_dev: int, k_dev: int, v_dev: int,
+                 alpha_dev: int, beta_dev: int, o_dev: int, stream: int = 0) -> None:
+    _check(lib().moe_gdn_step(ctypes.byref(shape), T, _p(state_dev), _p(q_dev), _p(k_dev), _p(v_dev), _p(alpha_dev),
+                              _p(beta_dev), _p(o_dev), _p(stream)))
 
 
 def moe_last_error() -> str:

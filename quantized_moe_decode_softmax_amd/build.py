@@ -25,7 +25,7 @@ TRACE_LIB = os.path.join(PKG, "libmoe_trace.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["gen.hip", "decode.hip", "stack1.hip", "noalloc.hip"]
+HIP_SOURCES = ["gen.hip", "decode.hip", "stack1.hip", "noalloc.hip", "dense.hip", "attention.hip", "gdn.hip"]
 HOST_SOURCES = ["moe_host.cpp"]
 HIP_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -70,6 +70,7 @@ struct Ptrs {
   float* wts;
   int* units;
   uint32_t* masks;
+  uint32_t* tmask;  // [T][k] rows of the call using the expert selected at (row, slot)
   uint16_t* a_hi;
   uint16_t* a_lo;
   float* ysh;  // shared expert's down projection [T][H] from the matrix-core path, or nullptr
@@ -332,8 +333,11 @@ __global__ void __launch_bounds__(256) route_kernel(Dims d, Ptrs p_, int n_rt) {
 // Routed experts for many token rows, one token row at a time per wave:
 // tasks are ordered (row t, slot, block of row pairs), a wave takes a run of
 // them, arranges x_t once per row and streams the gate/up rows of the row's
-// experts (an expert used by several rows is read once per row). The
-// arithmetic of a (row, pair) is the one of swiglu_task.
+// experts. An expert used by several rows is read once: the task of the
+// lowest row using it loads the block's rows and computes them for every row
+// in the expert's mask (arranging the other rows' inputs as it goes), and
+// the other rows' tasks for it do nothing. The arithmetic of a (row, pair) is
+// the one of swiglu_task whichever task computes it, so rows stay exact.
 template <int BITS, int CPL, int RP>
 __device__ __forceinline__ void swiglu_rows(const Dims& d, const Ptrs& p, int task0, int task1, int tps, int li,
                                             int lpr, int sr, int rpw) {
@@ -354,6 +358,8 @@ __device__ __forceinline__ void swiglu_rows(const Dims& d, const Ptrs& p, int ta
       }
     }
     const int e = p.ids[t * d.k + slot];
+    const uint32_t emask = p.tmask[t * d.k + slot];  // loaded beside the id, not after it
+    if ((int)__builtin_ctz(emask) != t) continue;  // a lower row's task computes this expert block
     const uint8_t* gate = p.layer + d.off_e0 + (int64_t)e * d.e_stride;
     const uint8_t* up = gate + d.off_e_up;
     const uint32_t* gsb = (const uint32_t*)(gate + cb);
@@ -387,6 +393,23 @@ __device__ __forceinline__ void swiglu_rows(const Dims& d, const Ptrs& p, int ta
       const float v = reduce_row(out[RP + q], lpr) * r;
       if (pairs[q] >= 0 && li == lpr - 1) store_a(d, p, t, slot, pairs[q], silu_mul(g, v));
     }
+    // the later rows using this expert, from the same loaded rows
+    for (uint32_t rest = emask & (emask - 1u); rest; rest &= rest - 1u) {
+      const int t2 = __builtin_ctz(rest);
+      int slot2 = 0;
+      for (int i = 0; i < d.k; ++i)
+        if (p.ids[t2 * d.k + i] == e) slot2 = i;
+      prep_x<BITS, CPL>(x, p.h_in + (int64_t)t2 * d.H, d.H, li, lpr);
+      const float r2 = p.rinv[t2];
+      cur_t = -1;  // x no longer holds row t (a second register set would cost a wave per SIMD)
+      dot_rows<BITS, CPL, R, 1>(Q, x, x, out);
+#pragma unroll
+      for (int q = 0; q < RP; ++q) {
+        const float g = reduce_row(out[q], lpr) * r2;
+        const float v = reduce_row(out[RP + q], lpr) * r2;
+        if (pairs[q] >= 0 && li == lpr - 1) store_a(d, p, t2, slot2, pairs[q], silu_mul(g, v));
+      }
+    }
   }
 }
 
@@ -396,6 +419,7 @@ __device__ __forceinline__ void swiglu_rows(const Dims& d, const Ptrs& p, int ta
 // row with the mask of rows using each. One workgroup of 1024 threads.
 __global__ void __launch_bounds__(1024) select_kernel(Dims d, Ptrs p) {
   __shared__ uint32_t s_emask[kMaxExperts];
+  __shared__ int s_ids[kMaxT * kMaxTopK];
   __shared__ int s_wcnt[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < d.E; e += 1024) s_emask[e] = 0u;
@@ -411,9 +435,11 @@ __global__ void __launch_bounds__(1024) select_kernel(Dims d, Ptrs p) {
       if (p.ids_out) p.ids_out[i] = my_id;
       if (p.w_out) p.w_out[i] = my_w;
       atomicOr(&s_emask[my_id], 1u << t);  // OR: the result does not depend on the order
+      s_ids[i] = my_id;
     }
   }
   __syncthreads();
+  for (int i = tid; i < d.T * d.k; i += 1024) p.tmask[i] = s_emask[s_ids[i]];
   // experts used by any row, ascending (E <= 1024: one per thread)
   const bool used = tid < d.E && s_emask[tid] != 0u;
   const unsigned long long bal = __ballot(used);
@@ -752,6 +778,7 @@ int32_t launch_layer(const LayerPlan& P, const WsMap& m, uint8_t* ws, const uint
   p.wts = (float*)(ws + m.wts);
   p.units = (int*)(ws + m.units);
   p.masks = (uint32_t*)(ws + m.masks);
+  p.tmask = (uint32_t*)(ws + m.tmask);
   p.a_hi = (uint16_t*)(ws + m.a_hi);
   p.a_lo = (uint16_t*)(ws + m.a_lo);
   p.ysh = nullptr;
@@ -812,6 +839,12 @@ int32_t finish(hipStream_t st, const uint32_t* status_dev) {
   }
   return MOE_OK;
 }
+
+}  // namespace
+
+int32_t debug_finish(moe_stream_t st) { return finish((hipStream_t)st, nullptr); }
+
+namespace {
 
 __global__ void write_table_kernel(const uint8_t** table, LayerBatch b, int n) {
   if ((int)threadIdx.x < n) table[threadIdx.x] = b.p[threadIdx.x];

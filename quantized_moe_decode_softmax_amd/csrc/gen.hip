@@ -228,3 +228,18 @@ extern "C" int32_t moe_generate_rows(uint64_t seed_x, int32_t T, int32_t H, uint
   if (e != hipSuccess) return set_error(MOE_ERR_HIP, "generator launch failed: %s", hipGetErrorString(e));
   return MOE_OK;
 }
+
+extern "C" int32_t moe_generate_matrix(int32_t bits, int32_t rows, int32_t cols, uint64_t seed, int32_t layer,
+                                       int32_t tensor, void* dst_dev, moe_stream_t stream) {
+  clear_error();
+  if (!bits_ok(bits)) return set_error(MOE_ERR_UNSUPPORTED, "bits %d not in {2,3,4,6,8}", bits);
+  if (rows < 1 || rows > (1 << 22) || cols < kGroup || cols > 65536 || cols % kGroup)
+    return set_error(MOE_ERR_INVALID_ARG, "rows %d / cols %d invalid", rows, cols);
+  if (tensor < 6 || tensor > 1023) return set_error(MOE_ERR_INVALID_ARG, "tensor id %d not in [6, 1023]", tensor);
+  if (layer < 0 || layer >= (1 << 20)) return set_error(MOE_ERR_INVALID_ARG, "layer %d out of range", layer);
+  if (!dst_dev) return set_error(MOE_ERR_INVALID_ARG, "dst_dev is NULL");
+  if ((uintptr_t)dst_dev % kAlign) return set_error(MOE_ERR_ALIGNMENT, "dst_dev must be 256-byte aligned");
+  int32_t rc = gen_matrix((uint8_t*)dst_dev, 0, 1, bits, rows, cols, seed, layer, (1 << 20) - 1, tensor,
+                          (hipStream_t)stream);
+  return rc ? rc : debug_finish(stream);
+}

@@ -54,6 +54,7 @@ struct WsMap {
   int64_t wts;          // float [T][k]
   int64_t units;        // int32 [1 + U] count, then expert ids of the unique units (ascending)
   int64_t masks;        // uint32 [U]   rows using each unit
+  int64_t tmask;        // uint32 [T][k] rows using the expert selected at (row, slot)
   int64_t a_hi;         // bf16  [T][k+1][Imax]  SwiGLU activations, high part
   int64_t a_lo;         // bf16  [T][k+1][Imax]  low part: a = hi + lo to 16 significant bits
   int64_t hbuf;         // bf16  [2][T][H] ping-pong for stacks
@@ -93,6 +94,9 @@ void clear_error();
 // MOE_DEBUG_SYNC=1 in the environment (read once): launching entry points
 // wait for their stream and report HIP errors and wait time-outs
 bool debug_sync();
+// With MOE_DEBUG_SYNC=1: wait for the stream, MOE_ERR_HIP on a HIP error;
+// else MOE_OK at once (device code files only).
+int32_t debug_finish(moe_stream_t st);
 
 int32_t check_shape(const moe_shape_t* s);
 

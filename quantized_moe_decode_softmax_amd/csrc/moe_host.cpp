@@ -91,6 +91,7 @@ WsMap ws_map(const moe_shape_t& s, int T) {
   m.wts = take((int64_t)T * k * 4);
   m.units = take((1 + U) * 4);
   m.masks = take(U * 4);
+  m.tmask = take((int64_t)T * k * 4);
   m.a_hi = take((int64_t)T * (k + 1) * imax * 2);
   m.a_lo = take((int64_t)T * (k + 1) * imax * 2);
   m.hbuf = take((int64_t)2 * T * s.hidden * 2);

@@ -342,3 +342,78 @@ def test_pack_rejects_out_of_range_code():
     with pytest.raises(moe.MoeError) as e:
         moe.moe_pack_matrix(4, codes, np.zeros((1, 1), np.uint16), np.zeros((1, 1), np.uint16))
     assert e.value.code == moe.MOE_ERR_INVALID_ARG
+
+
+def test_gemv_and_matrix_generator_argument_errors():
+    """moe_gemv / moe_generate_matrix validate on the host before any launch."""
+    A = 1 << 20
+    y = A * 64
+    for args, code in [((5, 128, 1, A, [(A * 16, 4, y)]), moe.MOE_ERR_UNSUPPORTED),
+                       ((8, 100, 1, A, [(A * 16, 4, y)]), moe.MOE_ERR_UNSUPPORTED),
+                       ((8, 16384, 1, A, [(A * 16, 4, y)]), moe.MOE_ERR_UNSUPPORTED),
+                       ((8, 128, 0, A, [(A * 16, 4, y)]), moe.MOE_ERR_INVALID_ARG),
+                       ((8, 128, 33, A, [(A * 16, 4, y)]), moe.MOE_ERR_INVALID_ARG),
+                       ((8, 128, 1, A, []), moe.MOE_ERR_INVALID_ARG),
+                       ((8, 128, 1, A, [(A * 16, 4, y)] * 5), moe.MOE_ERR_INVALID_ARG),
+                       ((8, 128, 1, A, [(A * 16 + 8, 4, y)]), moe.MOE_ERR_ALIGNMENT),
+                       ((8, 128, 1, A + 2, [(A * 16, 4, y)]), moe.MOE_ERR_ALIGNMENT),
+                       ((8, 128, 1, A, [(A * 16, 4, y + 2)]), moe.MOE_ERR_ALIGNMENT),
+                       ((8, 128, 1, A, [(A * 16, 0, y)]), moe.MOE_ERR_INVALID_ARG),
+                       ((8, 128, 1, A, [(0, 4, y)]), moe.MOE_ERR_INVALID_ARG),
+                       ((8, 128, 2, A, [(A * 16, 4, A + 4)]), moe.MOE_ERR_INVALID_ARG),   # output overlaps x
+                       ((8, 128, 1, A, [(A * 16, 8, y), (A * 32, 8, y + 16)]), moe.MOE_ERR_INVALID_ARG)]:
+        with pytest.raises(moe.MoeError) as e:
+            moe.moe_gemv(*args)
+        assert e.value.code == code, (args, e.value)
+    for args, code in [((5, 4, 64, 0, 0, 6, A * 16), moe.MOE_ERR_UNSUPPORTED),
+                       ((8, 0, 64, 0, 0, 6, A * 16), moe.MOE_ERR_INVALID_ARG),
+                       ((8, 4, 100, 0, 0, 6, A * 16), moe.MOE_ERR_INVALID_ARG),
+                       ((8, 4, 64, 0, 0, 5, A * 16), moe.MOE_ERR_INVALID_ARG),
+                       ((8, 4, 64, 0, -1, 6, A * 16), moe.MOE_ERR_INVALID_ARG),
+                       ((8, 4, 64, 0, 0, 6, A * 16 + 4), moe.MOE_ERR_ALIGNMENT)]:
+        with pytest.raises(moe.MoeError) as e:
+            moe.moe_generate_matrix(*args)
+        assert e.value.code == code, (args, e.value)
+
+
+def test_gqa_argument_errors():
+    A = 1 << 20
+    ok = moe.moe_attn_shape_t(16, 2, 256, 4096)
+    ws = moe.moe_gqa_workspace_bytes(ok, 3)
+    assert ws == ((4096 + 511) // 512) * 3 * 16 * (256 + 4) * 4
+    for sh, code in [(moe.moe_attn_shape_t(16, 2, 96, 4096), moe.MOE_ERR_UNSUPPORTED),
+                     (moe.moe_attn_shape_t(15, 2, 256, 4096), moe.MOE_ERR_UNSUPPORTED),
+                     (moe.moe_attn_shape_t(32, 2, 256, 4096), moe.MOE_ERR_UNSUPPORTED),  # 16 per KV head at d 256
+                     (moe.moe_attn_shape_t(16, 2, 256, 0), moe.MOE_ERR_INVALID_ARG)]:
+        with pytest.raises(moe.MoeError) as e:
+            moe.moe_gqa_workspace_bytes(sh, 1)
+        assert e.value.code == code
+    for args, code in [((ok, 0, 0, A, A * 2, A * 4, A * 8, A * 16, ws), moe.MOE_ERR_INVALID_ARG),
+                       ((ok, 9, 0, A, A * 2, A * 4, A * 8, A * 16, ws), moe.MOE_ERR_INVALID_ARG),
+                       ((ok, 3, 4094, A, A * 2, A * 4, A * 8, A * 16, ws), moe.MOE_ERR_INVALID_ARG),
+                       ((ok, 3, -1, A, A * 2, A * 4, A * 8, A * 16, ws), moe.MOE_ERR_INVALID_ARG),
+                       ((ok, 3, 0, 0, A * 2, A * 4, A * 8, A * 16, ws), moe.MOE_ERR_INVALID_ARG),
+                       ((ok, 3, 0, A + 2, A * 2, A * 4, A * 8, A * 16, ws), moe.MOE_ERR_ALIGNMENT),
+                       ((ok, 3, 0, A, A * 2, A * 4, A * 8, A * 16 + 16, ws), moe.MOE_ERR_ALIGNMENT),
+                       ((ok, 3, 0, A, A * 2, A * 4, A * 8, A * 16, ws - 1), moe.MOE_ERR_WORKSPACE)]:
+        with pytest.raises(moe.MoeError) as e:
+            moe.moe_gqa_decode(*args)
+        assert e.value.code == code, (args[1:3], e.value)
+
+
+def test_gdn_argument_errors():
+    A = 1 << 20
+    ok = moe.moe_gdn_shape_t(16, 32, 128, 128)
+    base = (ok, 1, A * 16, A, A * 2, A * 3, A * 4, A * 5, A * 64)
+    for over, code in [(dict(shape=moe.moe_gdn_shape_t(16, 32, 96, 128)), moe.MOE_ERR_UNSUPPORTED),
+                       (dict(shape=moe.moe_gdn_shape_t(16, 24, 128, 128)), moe.MOE_ERR_INVALID_ARG),
+                       (dict(shape=moe.moe_gdn_shape_t(16, 32, 128, 0)), moe.MOE_ERR_INVALID_ARG),
+                       (dict(T=0), moe.MOE_ERR_INVALID_ARG), (dict(T=33), moe.MOE_ERR_INVALID_ARG),
+                       (dict(state=0), moe.MOE_ERR_INVALID_ARG), (dict(state=A * 16 + 4), moe.MOE_ERR_ALIGNMENT),
+                       (dict(o=A * 16 + 1024), moe.MOE_ERR_INVALID_ARG)]:  # o inside the state
+        a = list(base)
+        for k, v in over.items():
+            a[{"shape": 0, "T": 1, "state": 2, "o": 8}[k]] = v
+        with pytest.raises(moe.MoeError) as e:
+            moe.moe_gdn_step(*a)
+        assert e.value.code == code, (over, e.value)
