@@ -165,8 +165,8 @@ def cpu_baseline(w, budget_s: float = 15.0):
 
 PHASES = ["layer start", "h staged", "phase A computed", "all logits seen", "top-k done",
           "routed loads issued", "routed pairs computed (wave 0)", "routed pairs computed (wave 7)",
-          "activations published", "first down inputs in LDS", "down rows done", "combine done",
-          "shared down inputs fetched (wave 7)"]
+          "routed activations stored", "first down inputs in LDS", "down rows done", "combine done",
+          "shared down inputs fetched (wave 7)", "down rows requested", "down rows in LDS"]
 
 
 def phase_trace(w, K: int, W: int) -> int:

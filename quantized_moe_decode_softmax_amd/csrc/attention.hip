@@ -10,8 +10,9 @@
 //                        weighted sum of values (online softmax), then combines
 //                        its four waves in a fixed order and stores
 //                        (max, sum, acc[d]) for the chunk;
-//   attn_combine_kernel  per (row, head): merges the chunks the row sees, in
-//                        ascending chunk order, and divides.
+//   attn_combine_kernel  per (row, head, 64 outputs): merges the chunks the
+//                        row sees in a grouping fixed by their number, and
+//                        divides.
 //
 // Split points are the fixed multiples of kChunk, and every sum runs in an
 // order fixed by the position alone, so a row of a T-row call equals a one-row
@@ -65,6 +66,63 @@ __device__ __forceinline__ void load_row(const uint16_t* base, uint32_t (&w)[D /
   }
 }
 
+// V batches: kVB positions of a wave, this lane's DL bf16 values of each,
+// kept raw until used.
+constexpr int kVB = 8;
+template <int DL>
+struct VRaw;
+template <>
+struct VRaw<4> { u32x2 w; };
+template <>
+struct VRaw<2> { uint32_t w; };
+template <>
+struct VRaw<1> { uint16_t w; };
+
+template <int D>
+__device__ __forceinline__ void load_vb(const uint16_t* vbase, int pw, int jb, int jlast, int lane,
+                                        VRaw<D / 64> (&vv)[kVB]) {
+  constexpr int DL = D / 64;
+#pragma unroll
+  for (int jj = 0; jj < kVB; ++jj) {
+    const int pj = pw + min(jb + jj, jlast);
+    const uint8_t* vr = (const uint8_t*)(vbase + (int64_t)pj * D + lane * DL);
+    if constexpr (DL == 4) vv[jj].w = gload<u32x2>(vr);
+    else if constexpr (DL == 2) vv[jj].w = gload<uint32_t>(vr);
+    else vv[jj].w = gload<uint16_t>(vr);
+  }
+}
+
+// acc[q][e] += p[position][q] * v[position][e] over one batch, positions in
+// order; p is the batch's first row of the wave's probabilities in LDS.
+template <int D, int QG>
+__device__ __forceinline__ void pv_batch(const float* p, const VRaw<D / 64> (&vv)[kVB],
+                                         float (&acc)[QG][D / 64]) {
+  constexpr int DL = D / 64;
+#pragma unroll
+  for (int jj = 0; jj < kVB; ++jj) {
+    float x[DL];
+    if constexpr (DL == 4) {
+      x[0] = bf16_lo_to_f32(vv[jj].w.x);
+      x[1] = bf16_hi_to_f32(vv[jj].w.x);
+      x[2] = bf16_lo_to_f32(vv[jj].w.y);
+      x[3] = bf16_hi_to_f32(vv[jj].w.y);
+    } else if constexpr (DL == 2) {
+      x[0] = bf16_lo_to_f32(vv[jj].w);
+      x[1] = bf16_hi_to_f32(vv[jj].w);
+    } else {
+      x[0] = __uint_as_float((uint32_t)vv[jj].w << 16);
+    }
+    asm volatile("" ::: "memory");  // one position's probabilities live at a time
+    float pq[QG];
+#pragma unroll
+    for (int qi = 0; qi < QG; ++qi) pq[qi] = p[jj * (QG + 1) + qi];
+#pragma unroll
+    for (int qi = 0; qi < QG; ++qi)
+#pragma unroll
+      for (int e = 0; e < DL; ++e) acc[qi][e] = fmaf(pq[qi], x[e], acc[qi][e]);
+  }
+}
+
 // G: query heads per KV head (compile time, so that a query slot's row and
 // head are constants); QG queries (RG whole rows of G heads) per pass.
 template <int D, int G>
@@ -73,7 +131,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a) 
   constexpr int RG = qg_of<D>() / G;
   constexpr int QG = RG * G;
   __shared__ uint32_t s_q[QG][D / 2];                  // the pass's queries (bf16 pairs)
-  __shared__ float s_p[kAttnWaves][64][QG];            // probabilities, by wave, position (lane), query
+  __shared__ float s_p[kAttnWaves][64][QG + 1];        // probabilities, by wave, position (lane), query
   __shared__ float s_ml[kAttnWaves][QG][2];            // per wave: running max, sum
   __shared__ float s_sc[kAttnWaves][QG];               // per wave: this step's rescale factor of each query
   __shared__ float s_acc[kAttnWaves - 1][QG][D];       // waves 1..3: weighted value sums
@@ -124,38 +182,57 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a) 
           s[qi] = dot2(kw[4 * i4 + 3], q4.w, s[qi]);
         }
       }
-      // online softmax over the wave's 64 positions: the masked scores go to
-      // LDS ([position][query]); lane qi then runs query qi over the 64
-      // positions in order (its maximum, the exponentials written back as
-      // probabilities, their sum) and publishes the rescale factor of the
-      // running sums. Slots of rows past the pass and masked positions get
-      // probability 0.
+      // masked scores to LDS ([position][query], rows padded by one word)
 #pragma unroll
       for (int qi = 0; qi < QG; ++qi) {
         const int r = qi / G;
         s_p[wave][lane][qi] = (r < nr && j <= lim0 + r) ? s[qi] * a.scale : -INFINITY;
       }
+      // weighted values: this lane's DL elements over the wave's 64 positions
+      // in batches of kVB positions, two batches' loads in flight (the first
+      // two are issued here, under the softmax). Positions past the last one
+      // a row of the pass sees have p = 0 and read the last seen row instead
+      // (the cache need not hold finite values beyond the rows' positions).
+      const int jlast = min(63, lim0 + nr - 1 - pw);  // >= 0 here
+      VRaw<DL> va[kVB], vb[kVB];
+      load_vb<D>(vbase, pw, 0, jlast, lane, va);
+      if (kVB <= jlast) load_vb<D>(vbase, pw, kVB, jlast, lane, vb);
       __builtin_amdgcn_wave_barrier();
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      if (lane < QG) {
+      // online softmax: lane (query qi = lane % QG, group gq = lane / QG)
+      // takes positions gq*QG .. gq*QG+QG-1 of query qi; maxima and sums are
+      // completed by butterflies over the groups (every lane of a query ends
+      // with the same values). The probabilities go back to LDS.
+      {
+        const int qi = lane % QG, gq = lane / QG;
+        float v[QG];
         float mw = -INFINITY;
-        for (int jj = 0; jj < 64; ++jj) mw = fmaxf(mw, s_p[wave][jj][lane]);
+#pragma unroll
+        for (int jj = 0; jj < QG; ++jj) {
+          v[jj] = s_p[wave][gq * QG + jj][qi];
+          mw = fmaxf(mw, v[jj]);
+        }
+#pragma unroll
+        for (int off = QG; off < 64; off <<= 1) mw = fmaxf(mw, __shfl_xor(mw, off));
         const float mn = fmaxf(m_lane, mw);
         float sc = 1.f, sum = 0.f;
         if (mn != -INFINITY) {
           sc = m_lane == -INFINITY ? 0.f : expf(m_lane - mn);
-          for (int jj = 0; jj < 64; ++jj) {
-            const float v = s_p[wave][jj][lane];
-            const float pj = v == -INFINITY ? 0.f : expf(v - mn);
-            s_p[wave][jj][lane] = pj;
+#pragma unroll
+          for (int jj = 0; jj < QG; ++jj) {
+            const float pj = v[jj] == -INFINITY ? 0.f : expf(v[jj] - mn);
+            s_p[wave][gq * QG + jj][qi] = pj;
             sum += pj;
           }
         } else {
-          for (int jj = 0; jj < 64; ++jj) s_p[wave][jj][lane] = 0.f;
+#pragma unroll
+          for (int jj = 0; jj < QG; ++jj) s_p[wave][gq * QG + jj][qi] = 0.f;
         }
+#pragma unroll
+        for (int off = QG; off < 64; off <<= 1) sum += __shfl_xor(sum, off);
         l_lane = l_lane * sc + sum;
         m_lane = mn;
-        s_sc[wave][lane] = sc;
+        if (gq == 0) s_sc[wave][qi] = sc;
       }
       __builtin_amdgcn_wave_barrier();
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -165,44 +242,13 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a) 
 #pragma unroll
         for (int e = 0; e < DL; ++e) acc[qi][e] *= sc;
       }
-      // weighted values: this lane's DL elements over the wave's 64 positions,
-      // in batches of kVB whose loads are all issued before the batch is
-      // used. Positions past the last one a row of the pass sees have p = 0
-      // and read the last seen row instead (the cache need not hold finite
-      // values beyond the rows' positions).
-      const int jlast = min(63, lim0 + nr - 1 - pw);  // >= 0 here
-      constexpr int kVB = 8;
 #pragma unroll 1
-      for (int jb = 0; jb <= jlast; jb += kVB) {
-        float vv[kVB][DL];
-#pragma unroll
-        for (int jj = 0; jj < kVB; ++jj) {
-          const int pj = pw + min(jb + jj, jlast);
-          const uint16_t* vr = vbase + (int64_t)pj * D + lane * DL;
-          if constexpr (DL == 4) {
-            const u32x2 x = gload<u32x2>((const uint8_t*)vr);
-            vv[jj][0] = bf16_lo_to_f32(x.x);
-            vv[jj][1] = bf16_hi_to_f32(x.x);
-            vv[jj][2] = bf16_lo_to_f32(x.y);
-            vv[jj][3] = bf16_hi_to_f32(x.y);
-          } else if constexpr (DL == 2) {
-            const uint32_t x = gload<uint32_t>((const uint8_t*)vr);
-            vv[jj][0] = bf16_lo_to_f32(x);
-            vv[jj][1] = bf16_hi_to_f32(x);
-          } else {
-            vv[jj][0] = __uint_as_float((uint32_t)gload<uint16_t>((const uint8_t*)vr) << 16);
-          }
-        }
-#pragma unroll
-        for (int jj = 0; jj < kVB; ++jj) {
-          asm volatile("" ::: "memory");  // one position's probabilities live at a time
-          float pq[QG];
-#pragma unroll
-          for (int qi = 0; qi < QG; ++qi) pq[qi] = s_p[wave][jb + jj][qi];
-#pragma unroll
-          for (int qi = 0; qi < QG; ++qi)
-#pragma unroll
-            for (int e = 0; e < DL; ++e) acc[qi][e] = fmaf(pq[qi], vv[jj][e], acc[qi][e]);
+      for (int jb = 0; jb <= jlast; jb += 2 * kVB) {
+        pv_batch<D, QG>(&s_p[wave][jb][0], va, acc);
+        if (jb + 2 * kVB <= jlast) load_vb<D>(vbase, pw, jb + 2 * kVB, jlast, lane, va);
+        if (jb + kVB <= jlast) {
+          pv_batch<D, QG>(&s_p[wave][jb + kVB][0], vb, acc);
+          if (jb + 3 * kVB <= jlast) load_vb<D>(vbase, pw, jb + 3 * kVB, jlast, lane, vb);
         }
       }
     }
@@ -255,51 +301,71 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a) 
   }
 }
 
+// One workgroup per (row, head, 64-element segment of the output). Wave w
+// takes the chunks w, w + kCombWaves, ... (kCombUnroll of them per round, all
+// loads of a round in flight) with a running maximum of its own; the waves'
+// sums are then rescaled to the common maximum and added in wave order. The
+// grouping depends only on the number of chunks the row sees, that is on its
+// position.
+constexpr int kCombWaves = 16;
+constexpr int kCombUnroll = 16;
+
 template <int D>
-__global__ void __launch_bounds__(64) attn_combine_kernel(AttnArgs a) {
-  constexpr int DL = D / 64;
-  const int lane = threadIdx.x;
-  const int t = blockIdx.x / a.n_q, h = blockIdx.x % a.n_q;
+__global__ void __launch_bounds__(64 * kCombWaves) attn_combine_kernel(AttnArgs a) {
+  __shared__ float s_m[kCombWaves];
+  __shared__ float s_l[kCombWaves];
+  __shared__ float s_o[kCombWaves][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x / a.n_q, h = blockIdx.x % a.n_q, e = blockIdx.y * 64 + lane;
   const int nc = (a.p0 + t) / kChunk + 1;
   const float* base = a.part + ((int64_t)t * a.n_q + h) * pstride<D>();
   const int64_t cs = (int64_t)a.T * a.n_q * pstride<D>();  // chunk stride
-  // the maximum over the chunks: lanes take chunks lane, lane + 64, ...
-  float M = -INFINITY;
-  for (int c = lane; c < nc; c += 64) M = fmaxf(M, base[c * cs]);
-  M = wave_max(M);
-  // the weighted sums, chunk by chunk in ascending order (8 chunks' loads in flight)
-  float L = 0.f, o[DL];
+  float mw = -INFINITY, L = 0.f, o = 0.f;
+  for (int c0 = wave; c0 < nc; c0 += kCombUnroll * kCombWaves) {
+    float mc[kCombUnroll], lc[kCombUnroll], xc[kCombUnroll];
 #pragma unroll
-  for (int e = 0; e < DL; ++e) o[e] = 0.f;
-  int c = 0;
-  for (; c + 8 <= nc; c += 8) {
-    float mc[8], lc[8], xc[8][DL];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float* pc = base + (c + u) * cs;
-      mc[u] = pc[0];
+    for (int u = 0; u < kCombUnroll; ++u) {
+      const int cu = c0 + u * kCombWaves;
+      const float* pc = base + (int64_t)min(cu, nc - 1) * cs;
+      mc[u] = cu < nc ? pc[0] : -INFINITY;
       lc[u] = pc[1];
-#pragma unroll
-      for (int e = 0; e < DL; ++e) xc[u][e] = pc[4 + lane * DL + e];
+      xc[u] = pc[4 + e];
     }
+    float mn = mw;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float f = expf(mc[u] - M);
+    for (int u = 0; u < kCombUnroll; ++u) mn = fmaxf(mn, mc[u]);
+    const float sc = mw == -INFINITY ? 0.f : expf(mw - mn);
+    L *= sc;
+    o *= sc;
+#pragma unroll
+    for (int u = 0; u < kCombUnroll; ++u) {
+      if (mc[u] == -INFINITY) continue;
+      const float f = expf(mc[u] - mn);
       L = fmaf(lc[u], f, L);
-#pragma unroll
-      for (int e = 0; e < DL; ++e) o[e] = fmaf(xc[u][e], f, o[e]);
+      o = fmaf(xc[u], f, o);
     }
+    mw = mn;
   }
-  for (; c < nc; ++c) {
-    const float* pc = base + c * cs;
-    const float f = expf(pc[0] - M);
-    L = fmaf(pc[1], f, L);
-#pragma unroll
-    for (int e = 0; e < DL; ++e) o[e] = fmaf(pc[4 + lane * DL + e], f, o[e]);
+  s_o[wave][lane] = o;
+  if (lane == 0) {
+    s_m[wave] = mw;
+    s_l[wave] = L;
   }
-  float* dst = a.o + ((int64_t)t * a.n_q + h) * D + lane * DL;
+  __syncthreads();
+  if (wave == 0) {
+    float M = s_m[0];
 #pragma unroll
-  for (int e = 0; e < DL; ++e) dst[e] = o[e] / L;
+    for (int w = 1; w < kCombWaves; ++w) M = fmaxf(M, s_m[w]);
+    float ot = 0.f, lt = 0.f;
+#pragma unroll
+    for (int w = 0; w < kCombWaves; ++w) {
+      if (s_m[w] == -INFINITY) continue;
+      const float f = expf(s_m[w] - M);
+      ot = fmaf(s_o[w][lane], f, ot);
+      lt = fmaf(s_l[w], f, lt);
+    }
+    a.o[((int64_t)t * a.n_q + h) * D + e] = ot / lt;
+  }
 }
 
 int64_t attn_ws_bytes(int n_q, int D, int T, int max_seq) {
@@ -376,7 +442,7 @@ extern "C" int32_t moe_gqa_decode(const moe_attn_shape_t* shape, int32_t T, int3
     MOE_ATTN_G(DD, 1) MOE_ATTN_G(DD, 2) MOE_ATTN_G(DD, 4) MOE_ATTN_G(DD, 8) \
     default: attn_partial_kernel<DD, (qg_of<DD>() >= 16 ? 16 : 8)><<<g1, kAttnThreads, 0, st>>>(a); break; \
   }                                                                      \
-  attn_combine_kernel<DD><<<T * a.n_q, 64, 0, st>>>(a);
+  attn_combine_kernel<DD><<<dim3(T * a.n_q, DD / 64), 64 * kCombWaves, 0, st>>>(a);
   switch (s.head_dim) {
     case 64: MOE_ATTN_D(64) break;
     case 128: MOE_ATTN_D(128) break;

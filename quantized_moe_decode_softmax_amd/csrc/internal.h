@@ -25,8 +25,11 @@ constexpr int kMaxLayersPerLaunch = 64;
 constexpr int kMaxLayers = 4096;
 constexpr uint32_t kStackMagic = 0x4D4F4553u;  // marks a moe_stack_t filled by moe_stack_init
 constexpr int64_t kAlign = 256;
-// copies of each exchange buffer of the streaming stack kernel (one per XCD)
-constexpr int kExchangeCopies = 8;
+// copies of each exchange buffer of the streaming stack kernel: a writer
+// stores every copy, workgroup w polls copy w % kExchangeCopies. Two measured
+// best at 256 workgroups (1, 2, 4, 8 and 16 were tried): fewer pollers per
+// line than one copy, fewer stores per word than more.
+constexpr int kExchangeCopies = 2;
 
 MOE_HD constexpr inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
@@ -66,7 +69,6 @@ struct WsMap {
   int64_t x_h;          // u64 [2][n_copy][H/2]      hidden state by layer parity
   int64_t x_logit;      // u64 [n_copy][E]           raw router dot products
   int64_t x_a;          // u64 [n_copy][k+1][Imax]   activations, bf16 hi | bf16 lo << 16
-  int64_t x_flag;       // u64 [n_copy][512]         per workgroup: its activations are stored
   int64_t xh_cs, xl_cs, xa_cs;
   int64_t status;       // u32 [64]           word 0: nonzero after a timed-out wait
   int64_t x_end;        // end of the region the streaming kernel clears per call

@@ -103,7 +103,6 @@ WsMap ws_map(const moe_shape_t& s, int T) {
   m.x_h = take(2 * m.n_copy * m.xh_cs * 8);
   m.x_logit = take(m.n_copy * m.xl_cs * 8);
   m.x_a = take(m.n_copy * m.xa_cs * 8);
-  m.x_flag = take(m.n_copy * 512 * 8);
   m.status = take(64 * 4);
   m.x_end = off;
 #ifdef MOE_PHASE_TRACE

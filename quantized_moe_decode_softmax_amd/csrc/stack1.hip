@@ -26,12 +26,8 @@
 // polls the words it needs until they carry the expected epoch, so the data
 // round trip is the synchronisation. Every buffer exists in n_copy copies; a
 // writer stores all of them and workgroup w reads copy w % n_copy, so that no
-// cache line is polled by every compute unit. The activations, which every
-// workgroup reads in full, are not polled while they are produced: each
-// workgroup sets a ready flag once it has stored its share, a consumer reads
-// the slot it needs once, waits for the flags of the workgroups that computed
-// it (one word per workgroup) and then reads again only the words whose tags
-// were not yet current.
+// cache line is polled by every compute unit. Each poll round re-reads only
+// the words whose tags were not yet current.
 //
 // Per layer and workgroup (8 waves, one workgroup per compute unit, as many
 // workgroups as the hidden state has slices of J rows):
@@ -44,18 +40,17 @@
 //      phase A) into LDS
 //   B  load (registers, at most two per wave, else the ring) and compute
 //      this workgroup's range of routed row pairs (k experts x I pairs split
-//      evenly over the grid), storing each activation as it is computed,
-//      then set the workgroup's ready flag; each wave then waits for the
-//      flags of the workgroups that computed the slot of its down task and
-//      reads that activation vector into LDS
-//   C  the shared expert's down rows (one task per wave, while the ready
-//      flags are awaited), the down-projection rows [j0, j0 + J) of the k
-//      experts (weights streamed through the ring during B, or right after
-//      the ready flag when B used registers), combine in rank order,
-//      residual, bf16, publish the slice of h_{l+1}
+//      evenly over the grid), storing each activation as it is computed;
+//      each wave then polls the activation vector of the slot of its down
+//      task into LDS
+//   C  the shared expert's down rows (one task per wave, before the routed
+//      activations are polled), the down-projection rows [j0, j0 + J) of the
+//      k experts (weights streamed through the ring during B, or right after
+//      it when B used registers), combine in rank order, residual, bf16,
+//      publish the slice of h_{l+1}
 //
-// Buffer reuse: every workgroup publishes a slice of h in every layer. Logits,
-// activations and flags of layer l+1 are written only by workgroups that have
+// Buffer reuse: every workgroup publishes a slice of h in every layer. Logits
+// and activations of layer l+1 are written only by workgroups that have
 // seen all of h_{l+1}, i.e. after every workgroup finished layer l (one buffer
 // each). h alternates between two buffers by layer parity: h_{l+2} is written
 // after its writer saw all of h_{l+1}, which every workgroup published after
@@ -91,9 +86,10 @@ constexpr int kMaxAWords = 12288;  // (k + 1) * imax
 // Slots of the per-phase timestamps of a phase-trace build (wave recording it):
 //  0 layer start (w0)            1 h staged in LDS (w0)        2 phase A computed (w0)
 //  3 all logits seen (w0)        4 top-k done (w0)             5 routed loads issued (w0)
-//  6 routed pairs computed (w0)  7 routed pairs computed (w7)  8 activations published (w0)
-//  9 first down slot's inputs in LDS (w0, after the ready flags)
+//  6 routed pairs computed (w0)  7 routed pairs computed (w7)  8 routed activations stored (w0)
+//  9 first down slot's inputs in LDS (w0)
 // 10 down rows done (w0)        11 combine done (thread 0)   12 shared down inputs fetched (w7)
+// 13 down rows requested (w0)   14 down rows in LDS (w0)
 constexpr int kPhases = 16;
 
 struct Args {
@@ -113,7 +109,6 @@ struct Args {
   uint64_t* x_h;      // [2][n_copy] copies of [H/2], stride h_cs
   uint64_t* x_logit;  // [n_copy] copies of [E], stride l_cs
   uint64_t* x_a;      // [n_copy] copies of [k+1][imax], stride a_cs
-  uint64_t* x_flag;   // [n_copy] copies of [512]
   int64_t h_cs, l_cs, a_cs;
   int n_copy;
   uint32_t* status;
@@ -447,6 +442,7 @@ struct Shared {
   // (S.r of the same layer is in place before the first of them)
   uint32_t rank_tag[kMaxTopK];
   uint32_t logit_ep;  // epoch of the layer whose logits wave 0 has seen (so all phase A output exists)
+  uint32_t sd_ep;     // epoch of the layer whose shared down rows and inputs are in S.sd / S.a
   uint64_t layers[kMaxLayersPerLaunch];  // the launch's layer blocks
 #ifdef MOE_PHASE_TRACE
   uint64_t ts[kPhases];  // this layer's phase timestamps (s_memrealtime, 100 MHz)
@@ -460,10 +456,17 @@ __shared__ Shared S;
 
 // Phase timestamps (builds with MOE_PHASE_TRACE only): lane 0 of the calling
 // wave stores the 100 MHz real-time counter in slot P of the layer's record.
+// The counter is read in inline assembly, together with its own wait, so
+// that the compiler adds no wait for the wave's outstanding memory operations
+// (it does for the builtin), which would change the timing being recorded.
 #ifdef MOE_PHASE_TRACE
-#define MOE_TS(P)                                                           \
-  do {                                                                      \
-    if ((threadIdx.x & 63) == 0) S.ts[P] = __builtin_amdgcn_s_memrealtime(); \
+#define MOE_TS(P)                                                                         \
+  do {                                                                                    \
+    if ((threadIdx.x & 63) == 0) {                                                        \
+      uint64_t t_;                                                                        \
+      asm volatile("s_memrealtime %0\n\ts_waitcnt lgkmcnt(0)" : "=s"(t_)::"memory");       \
+      S.ts[P] = t_;                                                                       \
+    }                                                                                     \
   } while (0)
 #else
 #define MOE_TS(P) \
@@ -545,18 +548,7 @@ __device__ __forceinline__ int n_b_tasks(const Args& a, const Ctx& c) {
 __device__ __forceinline__ bool split_b(const Ctx& c) {
   return c.rpw_h == 1 && (c.k & 1) == 0 && c.pb == 2 * kWaves && c.nwg * c.pb == c.k * c.I && c.I <= 64 * c.pb;
 }
-// The workgroups whose ready flags cover the activations of routed slot u.
-__device__ __forceinline__ void slot_producers(const Ctx& c, int u, int& w0, int& w1) {
-  if (split_b(c)) {
-    const int h = c.pb / 2, base = u < c.k / 2 ? 0 : c.k / 2 * c.I;
-    w0 = (u * c.I - base) / h;
-    w1 = ((u + 1) * c.I - 1 - base) / h;
-  } else {
-    w0 = u * c.I / c.pb;
-    w1 = ((u + 1) * c.I - 1) / c.pb;
-  }
-}
-// IdOf: the expert id of a rank (S.ids once the routing is complete).
+// IdOf: the expert id of a rank (see rank_id).
 template <int CPL_H, int CPL_I, class IdOf>
 __device__ __forceinline__ Task b_task(const Args& a, const Ctx& c, int i, const IdOf& id_of) {
   const int f0 = blockIdx.x * c.pb, f1 = min(c.k * c.I, f0 + c.pb);
@@ -594,10 +586,6 @@ __device__ __forceinline__ Task b_task(const Args& a, const Ctx& c, int i, const
   t.bytes = task_bytes(t.bits, t.K, t.n, true);
   return t;
 }
-template <int CPL_H, int CPL_I>
-__device__ __forceinline__ Task b_task(const Args& a, const Ctx& c, int i) {
-  return b_task<CPL_H, CPL_I>(a, c, i, [](int u) { return S.ids[u]; });
-}
 // The expert of rank u once wave 0's top-k has chosen it (this layer's tag).
 // On a time-out the stale id is still a valid expert (the status word says so).
 __device__ __forceinline__ int rank_id(const Args& a, const Ctx& c, int u) {
@@ -625,7 +613,8 @@ __device__ __forceinline__ int n_c_tasks(const Args& a, const Ctx& c) {
   const int de = down_task_rows(c.J, c.I, c.ebits);
   return c.k * ((c.J + de - 1) / de);
 }
-__device__ __forceinline__ Task c_task(const Args& a, const Ctx& c, int i) {
+template <class IdOf>
+__device__ __forceinline__ Task c_task(const Args& a, const Ctx& c, int i, const IdOf& id_of) {
   const int de = down_task_rows(c.J, c.I, c.ebits);
   const int tr = (c.J + de - 1) / de;
   const int j0 = blockIdx.x * c.J;
@@ -637,12 +626,13 @@ __device__ __forceinline__ Task c_task(const Args& a, const Ctx& c, int i) {
   t.slot = u;
   t.K = c.I;
   t.bits = c.ebits;
-  t.mat = c.layer + c.off_e0 + (int64_t)S.ids[u] * c.e_stride + c.off_e_down;
+  t.mat = c.layer + c.off_e0 + (int64_t)id_of(u) * c.e_stride + c.off_e_down;
   t.r0 = j0 + (i % tr) * de;
   t.n = min(de, min(j0 + c.J, c.H) - t.r0);
   t.bytes = task_bytes(t.bits, t.K, t.n, false);
   return t;
 }
+
 // the shared expert's down rows of this workgroup's slice
 // (one pass of a wave's row groups each, so that the waves share them)
 __host__ __device__ __forceinline__ int s_task_rows(int J, int Is) {
@@ -709,8 +699,7 @@ __device__ __forceinline__ void pair_rows(const Args& a, const Ctx& c, const Tas
   const float gv = reduce_row(pg, c.lpr_h) * rr;
   const float uv = reduce_row(pu, c.lpr_h) * rr;
   if (c.sr_h < t.n && c.li_h == c.lpr_h - 1) {
-    // stored at once (a routed pair's ready flag follows after the
-    // workgroup's last pair, by when these stores have long completed)
+    // stored at once: consumers poll these words themselves
     const int slot = t.kind == kSharedPair ? c.k : t.slot;
     st_copies(a.x_a + (int64_t)slot * c.imax + a_word(t.r0 + c.sr_h, c.imax), c.a_cs, c.n_copy,
               split_a(silu_mul(gv, uv)), c.ep);
@@ -752,10 +741,13 @@ __device__ __forceinline__ void pair_load(const Ctx& c, const Task& t, PairRegs<
     }
   }
 }
-// pair_rows on a task held in registers (the same sums in the same order).
+// pair_rows on a task held in registers (the same sums in the same order),
+// returning the activation word; store_pair publishes it. (Storing both
+// pairs only after computing both measured slower: the stores then meet the
+// down-row requests that follow them.)
 template <int CPL_H, int CPL_I, int BITS>
-__device__ __forceinline__ void pair_rows_reg(const Args& a, const Ctx& c, const Task& t, const PairRegs<BITS, CPL_H>& P,
-                                            const XLane<BITS, CPL_H>& x, float r) {
+__device__ __forceinline__ uint32_t pair_value_reg(const Ctx& c, const Task& t, const PairRegs<BITS, CPL_H>& P,
+                                                   const XLane<BITS, CPL_H>& x, float r) {
   float pg = 0.f, pu = 0.f;
   if (c.sr_h < t.n) {
 #pragma unroll
@@ -765,9 +757,11 @@ __device__ __forceinline__ void pair_rows_reg(const Args& a, const Ctx& c, const
   }
   const float gv = reduce_row(pg, c.lpr_h) * r;
   const float uv = reduce_row(pu, c.lpr_h) * r;
+  return split_a(silu_mul(gv, uv));
+}
+__device__ __forceinline__ void store_pair(const Args& a, const Ctx& c, const Task& t, uint32_t v) {
   if (c.sr_h < t.n && c.li_h == c.lpr_h - 1)
-    st_copies(a.x_a + (int64_t)t.slot * c.imax + a_word(t.r0 + c.sr_h, c.imax), c.a_cs, c.n_copy,
-              split_a(silu_mul(gv, uv)), c.ep);
+    st_copies(a.x_a + (int64_t)t.slot * c.imax + a_word(t.r0 + c.sr_h, c.imax), c.a_cs, c.n_copy, v, c.ep);
 }
 
 // The task's rows of one expert's down projection: the activation vector is
@@ -790,22 +784,29 @@ __device__ __forceinline__ void down_rows(const Args& a, const Ctx& c, const Tas
   }
 }
 
-// ---- phase A: all tasks of the wave fit in the ring (checked on the host)
+// ---- phase A: all tasks of the wave fit in the ring (checked on the host),
+// from byte `at` of the wave's ring (0, or the second half when phase A is
+// requested during the previous layer)
 template <int CPL_H, int CPL_I>
-__device__ __forceinline__ void phase_a_issue(const Args& a, const Ctx& c, int& n_instr) {
-  n_instr = 0;
+__device__ __forceinline__ void phase_a_issue(const Args& a, const Ctx& c, int at) {
   int off = 0;
-  const uint32_t base = lds_addr(S.ring[c.wave]);
+  const uint32_t base = lds_addr(S.ring[c.wave]) + at;
   for (int i = c.wave; i < n_a_tasks<CPL_H, CPL_I>(a, c); i += kWaves) {
     const Task t = a_task<CPL_H, CPL_I>(a, c, i);
-    n_instr += dma_task(t, base + off);
+    dma_task(t, base + off);
     off += t.bytes;
   }
 }
+template <int CPL_H, int CPL_I>
+__device__ __forceinline__ int phase_a_bytes(const Args& a, const Ctx& c) {
+  int n = 0;
+  for (int i = c.wave; i < n_a_tasks<CPL_H, CPL_I>(a, c); i += kWaves) n += a_task<CPL_H, CPL_I>(a, c, i).bytes;
+  return n;
+}
 template <int CPL_H, int CPL_I, int RB, int SB>
-__device__ __forceinline__ void phase_a_compute(const Args& a, const Ctx& c) {
+__device__ __forceinline__ void phase_a_compute(const Args& a, const Ctx& c, int at) {
   wait_vm(0);
-  int off = 0;
+  int off = at;
   for (int i = c.wave; i < n_a_tasks<CPL_H, CPL_I>(a, c); i += kWaves) {
     const Task t = a_task<CPL_H, CPL_I>(a, c, i);
     const uint8_t* buf = S.ring[c.wave] + off;
@@ -889,19 +890,13 @@ __device__ __forceinline__ void route(const Args& a, const Ctx& c, const uint32_
   if (c.lane == 0) S.sg = 1.0f / (1.0f + expf(-(r * gd)));
 }
 
-// ---- activations: this workgroup's ready flag, once every wave has stored
-// its routed activations (every wave calls this once, after its B tasks)
-__device__ __forceinline__ void publish_a(const Args& a, const Ctx& c) {
-  lds_barrier();
-  if (c.wave == 0 && c.lane == 0) st_copies(a.x_flag + blockIdx.x, 512, c.n_copy, 1u, c.ep);
-  if (c.wave == 0) MOE_TS(8);
-}
 
-// ---- the activation vector of one slot into S.a (one wave): for a routed
-// slot one read of every element, then the ready flags of the workgroups that
-// computed it (those whose pair ranges meet it), then the elements whose tags
-// were not yet current, until they are; the shared slot's activations were
-// stored in phase A and are polled directly.
+// ---- the activation vector of one slot into S.a (one wave): every element
+// is an epoch-tagged word, stored by the workgroup that computed its pair as
+// soon as it was computed; the words are read until all carry this layer's
+// epoch (each round re-reads only those that did not). No workgroup-wide
+// ready flag is needed, so no wave waits for the others of its workgroup
+// before its down rows.
 // NV >= K / 64: elements per lane.
 template <int NV>
 __device__ __forceinline__ void fetch_a(const Args& a, const Ctx& c, int slot) {
@@ -913,39 +908,7 @@ __device__ __forceinline__ void fetch_a(const Args& a, const Ctx& c, int slot) {
 #pragma unroll
   for (int j = 0; j < NV; ++j) want |= (c.lane + 64 * j < K ? 1u : 0u) << j;
   uint32_t v[NV];
-#pragma unroll
-  for (int j = 0; j < NV; ++j) v[j] = 0u;
-  uint32_t pending = want;
-  if (slot < c.k) {
-    // one read of the slot's words before the flags (up to 8 per lane; more
-    // would take registers the kernel lacks): most were stored as their pairs
-    // were computed, so only the late ones are read again below
-    uint64_t sv[NV <= 8 ? NV : 1];
-    if constexpr (NV <= 8) {
-#pragma unroll
-      for (int j = 0; j < NV; ++j) sv[j] = (want >> j & 1u) ? ld_tag(src + off(j)) : 0ull;
-    }
-    int w0, w1;
-    slot_producers(c, slot, w0, w1);
-    uint32_t fv[2];
-    const uint32_t fwant = (w0 + c.lane <= w1 ? 1u : 0u) | (w0 + c.lane + 64 <= w1 ? 2u : 0u);
-    poll<2>(a.x_flag + c.cp * 512 + w0 + c.lane, [](int m) { return (int64_t)64 * m; }, fwant, c.ep, fv, a.status);
-    if constexpr (NV <= 8) {
-#pragma unroll
-      for (int j = 0; j < NV; ++j)
-        if ((want >> j & 1u) && (uint32_t)(sv[j] >> 32) == c.ep) {
-          v[j] = (uint32_t)sv[j];
-          pending &= ~(1u << j);
-        }
-    }
-  }
-  if (pending) {
-    uint32_t pv[NV];
-    poll<NV>(src, off, pending, c.ep, pv, a.status);
-#pragma unroll
-    for (int j = 0; j < NV; ++j)
-      if (pending >> j & 1u) v[j] = pv[j];
-  }
+  poll<NV>(src, off, want, c.ep, v, a.status);
   uint32_t* dst = S.a + slot * c.imax;
 #pragma unroll
   for (int j = 0; j < NV; ++j)
@@ -968,9 +931,8 @@ __device__ __forceinline__ void wait_lds_epoch(const uint32_t* p, uint32_t epoch
 // inputs do not depend on the routing: the last wave streams the rows into
 // S.sd right after phase A and reads the shared activations (published in
 // phase A) once wave 0 has seen every logit (published after them), all
-// while wave 0 routes. The rows are computed, one task per wave, after each
-// wave has published its routed activations, while the waves wait for the
-// other workgroups' ready flags.
+// while wave 0 routes; S.sd_ep then says they are in place. The rows are
+// computed, one task per wave, after each wave's routed pairs.
 template <int NV>
 __device__ __forceinline__ void shared_down_fetch(const Args& a, const Ctx& c) {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -979,6 +941,8 @@ __device__ __forceinline__ void shared_down_fetch(const Args& a, const Ctx& c) {
   for (int i = 0; i < n_s_tasks(a, c); ++i) dma_task(s_task(a, c, i), base + i * tb);
   wait_lds_epoch(&S.logit_ep, c.ep, a.status);
   fetch_a<NV>(a, c, c.k);  // its waits also complete the weight loads above
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  lds_st(&S.sd_ep, c.ep);
 }
 template <int CPL_I, int SB, int KS>
 __device__ __forceinline__ void shared_down_part(const Args& a, const Ctx& c) {
@@ -993,8 +957,40 @@ __device__ __forceinline__ void shared_down_part(const Args& a, const Ctx& c) {
 // of the workgroup has at most this many)
 constexpr int kRegPairs = 2;
 
+// Whether the wave requests each next layer's phase A during the current
+// layer (into ring half 1): on the register path of phase B, when the wave's
+// C tasks fit in half 0 and its phase A tasks in half 1. Depends on the shape
+// only, so it holds for every layer of the launch.
+template <int CPL_H, int CPL_I>
+__device__ __forceinline__ bool prefetch_mode(const Args& a, const Ctx& c) {
+  if constexpr (CPL_H != 1) {
+    return false;
+  } else {
+    if (n_b_tasks<CPL_H, CPL_I>(a, c) > kRegPairs * kWaves) return false;
+    const int nc = n_c_tasks(a, c);
+    int cb = 0;
+    for (int i = c.wave; i < nc; i += kWaves) cb += c_task(a, c, i, [](int) { return 0; }).bytes;
+    return cb <= kHalf && phase_a_bytes<CPL_H, CPL_I>(a, c) <= kHalf;
+  }
+}
+
+// After the wave's routed pairs (whose activations it has stored): the
+// shared expert's down rows of the slice, once the last wave has them and
+// their inputs in LDS, and the complete routing for the C tasks.
+template <int CPL_I, int SB, int KS>
+__device__ __forceinline__ void after_b(const Args& a, const Ctx& c) {
+  if (c.wave == 0) MOE_TS(8);
+  wait_lds_epoch(&S.route_ep, c.ep, a.status);
+  wait_lds_epoch(&S.sd_ep, c.ep, a.status);
+  shared_down_part<CPL_I, SB, KS>(a, c);
+}
+
+// pre: phase A of the next layer (block `next_layer`, null after the launch's
+// last layer) is requested into the second ring half after the wave's last
+// activation poll (the C tasks then all sit in the first half, see
+// prefetch_mode), so that no later wait of this layer waits for it.
 template <int CPL_H, int CPL_I, int EB, int SB, int KI, int KS, int NV>
-__device__ __forceinline__ void phases_bc(const Args& a, const Ctx& c) {
+__device__ __forceinline__ void phases_bc(const Args& a, const Ctx& c, bool pre, const uint8_t* next_layer) {
   const int nb = n_b_tasks<CPL_H, CPL_I>(a, c), nc = n_c_tasks(a, c);
   // the wave's tasks: B tasks c.wave, c.wave + 8, ..., then C tasks likewise
   int mb = nb > c.wave ? (nb - c.wave + kWaves - 1) / kWaves : 0;
@@ -1009,7 +1005,7 @@ __device__ __forceinline__ void phases_bc(const Args& a, const Ctx& c) {
     auto id_of = [&](int u) { return rank_id(a, c, u); };
     // B from registers: the wave's routed pairs are requested at once with
     // global loads (a burst of a few KB per wave arrives about twice as soon
-    // that way as through LDS), computed, and published; only then are the
+    // that way as through LDS) and computed; only then are the
     // down rows of phase C streamed into the ring, so that no wait for the
     // pairs also waits for them (both complete in issue order).
     MOE_T1_BITS(EB, c.ebits, B, {
@@ -1026,23 +1022,25 @@ __device__ __forceinline__ void phases_bc(const Args& a, const Ctx& c) {
       if (c.wave == 0) MOE_TS(5);
       XLane<B, CPL_H> x;
       h_lane<B, CPL_H>(S.h, c.H, c.li_h, c.lpr_h, x);
-      if (mb > 0) pair_rows_reg<CPL_H, CPL_I, B>(a, c, t0, P0, x, S.r);
-      if (mb > 1) pair_rows_reg<CPL_H, CPL_I, B>(a, c, t1, P1, x, S.r);
+      if (mb > 0) store_pair(a, c, t0, pair_value_reg<CPL_H, CPL_I, B>(c, t0, P0, x, S.r));
+      if (mb > 1) store_pair(a, c, t1, pair_value_reg<CPL_H, CPL_I, B>(c, t1, P1, x, S.r));
+      // every pair load has been waited for above, on whichever path; saying
+      // so here, where all paths meet, keeps the compiler from waiting for
+      // the stores below before it reuses a load's registers
+
       if (c.wave == 0) MOE_TS(6);
       if (c.wave == kWaves - 1) MOE_TS(7);
     });
     mb = 0;
   }
   const int m = mb + mc;
+  // experts by their rank tags: on the register path the C tasks are
+  // requested before the wave knows that the routing is complete
+  auto rid = [&](int u) { return rank_id(a, c, u); };
   auto task = [&](int j) {
-    return j < mb ? b_task<CPL_H, CPL_I>(a, c, c.wave + kWaves * j) : c_task(a, c, c.wave + kWaves * (j - mb));
+    return j < mb ? b_task<CPL_H, CPL_I>(a, c, c.wave + kWaves * j, rid) : c_task(a, c, c.wave + kWaves * (j - mb), rid);
   };
   bool exchanged = false;
-  if (reg_b) {  // phase B is done: publish before streaming phase C
-    publish_a(a, c);
-    shared_down_part<CPL_I, SB, KS>(a, c);
-    exchanged = true;
-  }
   const uint32_t base = lds_addr(S.ring[c.wave]);
   // batches of whole tasks in the two halves: tasks [bs, be), bn instructions
   int bs0 = 0, be0 = 0, bn0 = 0, bs1 = 0, be1 = 0, bn1 = 0;
@@ -1060,19 +1058,31 @@ __device__ __forceinline__ void phases_bc(const Args& a, const Ctx& c) {
     }
     be = next;
   };
+  auto prefetch_next = [&]() {
+    if (pre && next_layer) {
+      Ctx cn = c;
+      cn.layer = next_layer;
+      phase_a_issue<CPL_H, CPL_I>(a, cn, kHalf);
+    }
+  };
   fill(0, bs0, be0, bn0);
   fill(1, bs1, be1, bn1);
+  if (c.wave == 0) MOE_TS(13);
+  if (reg_b) {  // phase B is done; the down rows requested above arrive meanwhile
+    after_b<CPL_I, SB, KS>(a, c);
+    exchanged = true;
+  }
   int fetched = -1;  // slot whose activations this wave holds in S.a
   for (int b = 0;; ++b) {
     const int h = b & 1;
     const int j0 = h ? bs1 : bs0, j1 = h ? be1 : be0;
     if (j0 == j1) break;
     wait_vm(h ? bn0 : bn1);  // the other half's batch was issued after this one
+    if (c.wave == 0 && b == 0) MOE_TS(14);
     int off = 0;
     for (int j = j0; j < j1; ++j) {
       if (j == mb && !exchanged) {
-        publish_a(a, c);
-        shared_down_part<CPL_I, SB, KS>(a, c);
+        after_b<CPL_I, SB, KS>(a, c);
         exchanged = true;
       }
       const Task t = task(j);
@@ -1081,6 +1091,7 @@ __device__ __forceinline__ void phases_bc(const Args& a, const Ctx& c) {
         if (c.wave == 0 && fetched < 0) MOE_TS(9);
         fetched = t.slot;
       }
+      if (j == m - 1) prefetch_next();  // the wave's last poll is done
       const uint8_t* buf = S.ring[c.wave] + h * kHalf + off;
       if (t.kind == kRoutedPair) {
         MOE_T1_BITS(EB, c.ebits, B, {
@@ -1089,8 +1100,7 @@ __device__ __forceinline__ void phases_bc(const Args& a, const Ctx& c) {
           pair_rows<CPL_H, CPL_I, B>(a, c, t, buf, x, S.r);
         });
         if (j + 1 == mb) {  // the wave's last routed pair: publish without waiting for the next batch
-          publish_a(a, c);
-          shared_down_part<CPL_I, SB, KS>(a, c);
+          after_b<CPL_I, SB, KS>(a, c);
           exchanged = true;
         }
       } else {
@@ -1102,10 +1112,8 @@ __device__ __forceinline__ void phases_bc(const Args& a, const Ctx& c) {
     if (h) fill(1, bs1, be1, bn1);
     else fill(0, bs0, be0, bn0);
   }
-  if (!exchanged) {
-    publish_a(a, c);
-    shared_down_part<CPL_I, SB, KS>(a, c);
-  }
+  if (!exchanged) after_b<CPL_I, SB, KS>(a, c);
+  if (m == 0) prefetch_next();
 }
 
 // ---- combine: h_{l+1}[j] = bf16(h_l[j] + sum_i w_i y_i[j] + sg y_s[j])
@@ -1221,26 +1229,33 @@ __global__ void __launch_bounds__(kThreads) stack1_kernel(Args a) {
   c.li_h = c.lane % c.lpr_h;
   c.sr_h = c.lane / c.lpr_h;
   c.cp = blockIdx.x % c.n_copy;
-  if (threadIdx.x == 0) S.route_ep = S.logit_ep = 0u;  // ordered before their readers by the barrier below
-  if (threadIdx.x < kMaxTopK) S.rank_tag[threadIdx.x] = 0u;
+  if (threadIdx.x == 0) S.route_ep = S.logit_ep = S.sd_ep = 0u;  // ordered before their readers by the barrier below
+  if (threadIdx.x < kMaxTopK) {
+    S.rank_tag[threadIdx.x] = 0u;
+    S.ids[threadIdx.x] = 0;
+  }
   if ((int)threadIdx.x < a.n_layers)
     S.layers[threadIdx.x] = (uint64_t)(a.table ? a.table[a.l0 + threadIdx.x] : a.layers[threadIdx.x]);
   lds_barrier();
+  auto layer_at = [](int l) {
+    const uint64_t lp = S.layers[l];
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)lp);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(lp >> 32));
+    return (const uint8_t*)(((uint64_t)hi << 32) | lo);
+  };
+  c.layer = layer_at(0);
+  const bool pre = prefetch_mode<CPL_H, CPL_I>(a, c);
+  const int a_at = pre ? kHalf : 0;  // where phase A lands in the wave's ring
   for (int l = 0; l < a.n_layers; ++l) {
 #ifdef MOE_PHASE_TRACE
     if (threadIdx.x < kPhases) S.ts[threadIdx.x] = 0u;  // phases a path does not pass stay 0
 #endif
     if (c.wave == 0) MOE_TS(0);
-    {
-      const uint64_t lp = S.layers[l];
-      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)lp);
-      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(lp >> 32));
-      c.layer = (const uint8_t*)(((uint64_t)hi << 32) | lo);
-    }
+    c.layer = layer_at(l);
     c.ep = (uint32_t)l + 1;
-    // phase A weights stream in while h_l is polled
-    int na;
-    phase_a_issue<CPL_H, CPL_I>(a, c, na);
+    // phase A weights stream in while h_l is polled (requested during the
+    // previous layer in prefetch mode)
+    if (!pre || l == 0) phase_a_issue<CPL_H, CPL_I>(a, c, a_at);
     uint32_t gvn[CPL_H][16];
     if (c.wave == 0) {
       const uint16_t* gv = (const uint16_t*)(c.layer + c.off_gatevec);
@@ -1258,7 +1273,7 @@ __global__ void __launch_bounds__(kThreads) stack1_kernel(Args a) {
     stage_h(a, c, l);
     lds_barrier();
     if (c.wave == 0) MOE_TS(1);
-    phase_a_compute<CPL_H, CPL_I, RB, SB>(a, c);
+    phase_a_compute<CPL_H, CPL_I, RB, SB>(a, c, a_at);
     if (c.wave == 0) {
       MOE_TS(2);
     if constexpr (ME != 0) {
@@ -1282,7 +1297,7 @@ __global__ void __launch_bounds__(kThreads) stack1_kernel(Args a) {
       if (a.ids_out) a.ids_out[(int64_t)l * c.k + threadIdx.x] = S.ids[threadIdx.x];
       if (a.w_out) a.w_out[(int64_t)l * c.k + threadIdx.x] = S.w[threadIdx.x];
     }
-    phases_bc<CPL_H, CPL_I, EB, SB, SH::KI, SH::KS, SH::NV>(a, c);
+    phases_bc<CPL_H, CPL_I, EB, SB, SH::KI, SH::KS, SH::NV>(a, c, pre, l + 1 < a.n_layers ? layer_at(l + 1) : nullptr);
     if (c.wave == 0) MOE_TS(10);
     lds_barrier();
     combine(a, c, l);
@@ -1406,7 +1421,6 @@ int32_t launch_stack_t1(const moe_shape_t& s, const moe_layer_layout_t& L, const
   a.x_h = (uint64_t*)(ws + m.x_h);
   a.x_logit = (uint64_t*)(ws + m.x_logit);
   a.x_a = (uint64_t*)(ws + m.x_a);
-  a.x_flag = (uint64_t*)(ws + m.x_flag);
   a.h_cs = m.xh_cs;
   a.l_cs = m.xl_cs;
   a.a_cs = m.xa_cs;
