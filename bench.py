@@ -24,7 +24,12 @@ row per step (seed 1000 + step). Prints one JSON line:
 * step_us: median, 10th and 90th percentile of the per-step call durations
   (the same HIP events); unique_experts_per_layer: the mean size of the union
   of the rows' selected experts per layer and step;
-* cpu_baseline: the fp64 oracle timed on this host on a bounded sample.
+* config0_gpu (a3b only): GPU microseconds per layer of the small one-layer
+  shape through the same entry point;
+* cpu_baseline: the fp64 oracle timed on this host on a bounded sample, single
+  core (value) and all cores, split into compute and weight regeneration per
+  layer, for the bench workload and the one-layer and 397B-A17B shapes, with
+  the CPU model, os.cpu_count(), the affinity-mask cores and BLAS threads.
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload a3b] [--no-cpu]
        python bench.py --copy-probe MIB   (PMC calibration: 5 device copies)
@@ -45,7 +50,7 @@ import numpy as np
 
 HBM_PEAK_GBPS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ["stack1.hip", "gemv.h", "device_common.h"]  # the stack kernel's device code
+KERNEL_SOURCES = ["stack1.hip", "gemv.h", "device_common.h", "internal.h"]  # the stack kernel's device code
 
 # HBM traffic of one stack-kernel launch, from two rocprofv3 --pmc passes
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) over
@@ -118,49 +123,126 @@ def touched_bytes(w, ids: np.ndarray) -> int:
     return total
 
 
-def cpu_baseline(w, budget_s: float = 15.0):
-    """The oracle as it stands: token rows through the layer stack, in order, until the budget is spent."""
+def _host_info():
+    """CPU model, os.cpu_count() and the cores of this process's affinity mask."""
+    model = None
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        aff = os.cpu_count()
+    return model, os.cpu_count(), aff
+
+
+def _oracle_pass(w, threads: int, budget_s: float):
+    """The oracle as it stands: token rows through w's layer stack in order,
+    BLAS limited to `threads`, until the budget is spent (at least one layer).
+    Each layer runs twice on the same input: the first pass regenerates from
+    the seed the weights the layer touches, the second reuses them, so the
+    difference is the regeneration time. Returns per-layer means."""
     import oracle
     from oracle.gen import GeneratedLayer, MoEShape, gen_x
+    from threadpoolctl import threadpool_info, threadpool_limits
 
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
     sh = MoEShape(hidden=w.hidden, n_experts=w.n_experts, inter=w.inter, top_k=w.top_k,
                   shared_inter=w.shared_inter, router_bits=w.router_bits, expert_bits=w.expert_bits,
                   shared_bits=w.shared_bits, eps=w.rms_eps)
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    if ctx:
-        ctx.__enter__()
-    try:
-        t0 = time.perf_counter()
-        n = 0  # layer passes done
-        tokens = 0
-        while time.perf_counter() - t0 < budget_s:
-            h = gen_x(1000 + tokens, 1, w.hidden)
+    with threadpool_limits(limits=threads):
+        blas = sorted({i["num_threads"] for i in threadpool_info()})
+        t_start = time.perf_counter()
+        comp = regen = 0.0
+        n = token = 0
+        done = False
+        while not done:
+            h = gen_x(1000 + token, 1, w.hidden)
             for layer in range(w.n_layers):
-                r = oracle.layer_forward(GeneratedLayer(sh, 0, layer), h)
-                h = oracle.bf16_round(r["y"])
+                gl = GeneratedLayer(sh, 0, layer)
+                t0 = time.perf_counter()
+                oracle.layer_forward(gl, h)
+                t1 = time.perf_counter()
+                r = oracle.layer_forward(gl, h)
+                t2 = time.perf_counter()
+                comp += t2 - t1
+                regen += max(0.0, (t1 - t0) - (t2 - t1))
                 n += 1
-                if time.perf_counter() - t0 > budget_s:
+                h = oracle.bf16_round(r["y"])
+                if time.perf_counter() - t_start > budget_s:
+                    done = True
                     break
-            tokens += 1
-        dt = time.perf_counter() - t0
-    finally:
-        if ctx:
-            ctx.__exit__(None, None, None)
-    per_token = dt / n * w.n_layers
+            token += 1
+    per_token = (comp + regen) / n * w.n_layers
+    return {"tok_s": round(1.0 / per_token, 5), "s_per_token": round(per_token, 3),
+            "compute_s_per_layer": round(comp / n, 4), "regen_s_per_layer": round(regen / n, 4),
+            "layers_timed": n, "layers_per_token": w.n_layers, "blas_threads": blas,
+            "extrapolated": n < w.n_layers}
+
+
+def cpu_baseline(w, budget_s: float = 10.0):
+    """The oracle timed on this host, single core and all cores, for the bench
+    workload and for the small one-layer shape and the 397B-A17B shape."""
+    from quantized_moe_decode_softmax_amd import WORKLOADS
+
+    model, n_cpu, aff = _host_info()
+    one = _oracle_pass(w, 1, budget_s)
+    allc = _oracle_pass(w, aff, budget_s)
+    others = {}
+    for name, share in (("tiny", 0.2), ("a17b", 1.0)):
+        if name == w.name:
+            continue
+        ow = WORKLOADS[name]
+        others[name] = {"single_core": _oracle_pass(ow, 1, budget_s * share),
+                        "all_cores": dict(_oracle_pass(ow, aff, budget_s * share), cores=aff)}
     return {
-        "value": 1.0 / per_token,
+        "value": one["tok_s"],
         "unit": "tok/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"{n} layer passes ({tokens} token(s), x seeds from 1000, through the {w.n_layers}-layer "
-                   f"stack in order) in {dt:.1f} s, fp64 numpy incl. regenerating the selected experts, BLAS "
-                   f"limited to 1 thread; scaled to {w.n_layers} layers per token"),
-        "host_cpus": os.cpu_count(),
+        "sample": (f"{one['layers_timed']} layer passes of the {w.n_layers}-layer {w.name} stack (token rows from "
+                   f"x seed 1000, layers in order), fp64 numpy, BLAS limited to 1 thread; per layer "
+                   f"{one['compute_s_per_layer']} s of steps O2-O8 plus {one['regen_s_per_layer']} s regenerating "
+                   f"the touched weights from the seed; scaled to {w.n_layers} layers per token"),
+        "single_core": one,
+        "all_cores": dict(allc, cores=aff),
+        "other_configs": others,
+        "cpu_model": model,
+        "os_cpu_count": n_cpu,
+        "affinity_cores": aff,
     }
+
+
+def config0_gpu(K: int = 200, W: int = 20):
+    """GPU time per layer of the small one-layer shape (moe_stack_decode, T = 1)."""
+    import torch
+
+    from quantized_moe_decode_softmax_amd import WORKLOADS
+    from quantized_moe_decode_softmax_amd import _lib as Lb
+    from quantized_moe_decode_softmax_amd.runtime import DeviceStack
+
+    w = WORKLOADS["tiny"]
+    ds = DeviceStack.from_workload(w)
+    st = ds.state()
+    stream = torch.cuda.current_stream().cuda_stream
+    out = torch.empty((1, w.hidden), dtype=torch.bfloat16, device="cuda")
+    xs = [ds.rows(1000 + s, 1) for s in range(W + K)]
+    for s in range(W):
+        Lb.moe_stack_decode(st, 1, xs[s].data_ptr(), out.data_ptr(), None, None, None, stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * K)]
+    for s in range(K):
+        ev[2 * s].record()
+        Lb.moe_stack_decode(st, 1, xs[W + s].data_ptr(), out.data_ptr(), None, None, None, stream)
+        ev[2 * s + 1].record()
+    torch.cuda.synchronize()
+    us = np.array([ev[2 * s].elapsed_time(ev[2 * s + 1]) for s in range(K)]) * 1e3 / w.n_layers
+    return {"workload": "tiny: 1 layer, H 256, 16 experts of I 128, top-2 + shared, 4-bit experts, bf16 router, T=1",
+            "us_per_layer": {"median": round(float(np.median(us)), 2), "p10": round(float(np.percentile(us, 10)), 2),
+                             "p90": round(float(np.percentile(us, 90)), 2)}}
 
 
 PHASES = ["layer start", "h staged", "phase A computed", "all logits seen", "top-k done",
@@ -460,7 +542,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="a3b")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time per measured mode")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
     ap.add_argument("--rows", type=int, default=0, help="token rows per step (default: the workload's T)")
     ap.add_argument("--phase-trace", action="store_true", help="per-phase timestamps (phase-trace build)")
@@ -588,6 +670,8 @@ def main() -> int:
             "traffic_detail": traffic_detail,
         },
     }
+    if args.workload == "a3b" and not args.rows:
+        res["config0_gpu"] = config0_gpu()
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(res), flush=True)
