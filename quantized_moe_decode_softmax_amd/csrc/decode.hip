@@ -413,6 +413,16 @@ __device__ __forceinline__ void swiglu_rows(const Dims& d, const Ptrs& p, int ta
   }
 }
 
+// Largest T at which the routed gate/up kernel reads a shared expert once
+// for all rows using it. Its task then arranges each further row's input in
+// the registers that held its own row's, which the wave's next task (of the
+// same row) must arrange again: at T = 8 (35B-A3B shape) the single read
+// costs no time, at T = 32 (397B-A17B low-bit shape, 113 distinct experts of
+// 128 selections per layer) it took the kernel from 171 to 259 us per layer
+// against 12% fewer bytes, so there each row reads its expert itself (the
+// down projections still read each distinct expert once).
+constexpr int kShareMaxT = 8;
+
 // ---------------------------------------------------------- select kernel
 // Routing of the call, once: top-k of every token row (row t on wave t % 16),
 // the renormalised weights, and the ascending list of experts used by any
@@ -439,7 +449,11 @@ __global__ void __launch_bounds__(1024) select_kernel(Dims d, Ptrs p) {
     }
   }
   __syncthreads();
-  for (int i = tid; i < d.T * d.k; i += 1024) p.tmask[i] = s_emask[s_ids[i]];
+  // rows sharing the expert of (row, slot): computed by the lowest row's
+  // task from one read of the expert's rows, up to kShareMaxT rows; above
+  // that every (row, slot) reads its expert itself (see kShareMaxT)
+  for (int i = tid; i < d.T * d.k; i += 1024)
+    p.tmask[i] = d.T <= kShareMaxT ? s_emask[s_ids[i]] : 1u << (i / d.k);
   // experts used by any row, ascending (E <= 1024: one per thread)
   const bool used = tid < d.E && s_emask[tid] != 0u;
   const unsigned long long bal = __ballot(used);
