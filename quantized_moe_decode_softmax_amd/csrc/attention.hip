@@ -2,14 +2,17 @@
 // i = 0..T-1 at positions p0 + i attend causally to the cache, query head h
 // to KV head h / g. moe_gqa_decode computes it in two kernels:
 //
-//   attn_partial_kernel  one workgroup per (chunk of kChunk positions, KV head):
-//                        the chunk's keys and values are read for every query
-//                        head of that KV head and (in passes of up to kQG
-//                        queries) every verify row; per (row, head) it keeps
-//                        the running maximum, the sum of exponentials and the
-//                        weighted sum of values (online softmax), then combines
-//                        its four waves in a fixed order and stores
-//                        (max, sum, acc[d]) for the chunk;
+//   partial kernel       one workgroup per (chunk of kChunk positions, KV head)
+//                        keeps, per (row, head), the running maximum, the sum
+//                        of exponentials and the weighted sum of values
+//                        (online softmax) and stores (max, sum, acc[d]) for
+//                        the chunk. Head dimension 256 (the card's shape):
+//                        attn_mq_kernel, every verify row in one pass, the
+//                        scores of all queries on the matrix cores, so the
+//                        chunk's K and V are read once for all query heads
+//                        and all verify rows. Head dimensions 64 and 128:
+//                        attn_partial_kernel, passes of up to kQG queries on
+//                        the vector units (a pass per group of verify rows);
 //   attn_combine_kernel  per (row, head, 64 outputs): merges the chunks the
 //                        row sees in a grouping fixed by their number, and
 //                        divides.
@@ -21,8 +24,9 @@
 // split-K with split points and summation order that depend only on the row's
 // position). Shapes of the card ("Beyond this checkpoint"): 16 query heads,
 // 2 KV heads, head dimension 256; bf16 KV cache ("Hardware"). Scores are the
-// bf16 products of q and k accumulated in fp32 by v_dot2c_f32_bf16, scaled by
-// 1/sqrt(d); probabilities and the output are fp32.
+// bf16 products of q and k accumulated in fp32 (v_dot2c_f32_bf16, or the
+// matrix cores at head dimension 256), scaled by 1/sqrt(d); probabilities and
+// the output are fp32.
 #include <cmath>
 
 #include "gemv.h"
@@ -301,6 +305,178 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a) 
   }
 }
 
+// ---- head dimension 256: every verify row in one pass over the chunk.
+// The scores of all T x G queries of a KV head are one small dense product
+// per 16 positions, Q [queries x 256] times K^T [256 x 16 positions], on the
+// matrix cores (v_mfma_f32_16x16x32_bf16: exact bf16 products, fp32 sums),
+// so K and V are read once for all query heads and all verify rows (the
+// card's "How it works"). Per step of 64 positions: wave w computes the
+// scores of positions [16w, 16w + 16) of the step for every query tile and
+// writes them, scaled and masked, to LDS; wave w then runs the online
+// softmax of queries w, w + 4, ... over the 64 positions (wave-wide max and
+// sum in a fixed tree) and writes their probabilities [position][query] and
+// rescale factors; finally each lane of the workgroup owns one of the 256
+// output dimensions and accumulates p * v over the step's positions for
+// every query (each V row read once, 128 bytes per wave). A query's result
+// depends only on its own row's data: steps past a row's position add
+// exactly nothing (p = 0, rescale 1), so a verify row equals a one-row call.
+typedef __bf16 at_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float at_f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kMqStep = 64;  // positions per step (16 per wave)
+
+__device__ __forceinline__ at_f32x4 mfma_qk(u32x4 a, u32x4 b, at_f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(at_bf16x8, a), __builtin_bit_cast(at_bf16x8, b),
+                                                 c, 0, 0, 0);
+}
+
+// Workgroup barrier for LDS data only: the global loads in flight (the
+// next step's keys, this step's values) are not waited for, as
+// __syncthreads would.
+__device__ __forceinline__ void mq_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int G, int QP>
+__global__ void __launch_bounds__(kAttnThreads) attn_mq_kernel(AttnArgs a) {
+  constexpr int D = 256;
+  constexpr int QPW = QP / kAttnWaves;  // softmax queries per wave
+  __shared__ __attribute__((aligned(16))) uint32_t s_q[QP][D / 2 + 4];  // bf16 pairs; rows padded by 16 bytes
+  __shared__ float s_s[QP][kMqStep + 1];                               // scaled, masked scores [query][position]
+  __shared__ __attribute__((aligned(16))) float s_pt[kMqStep][QP + 4];  // probabilities [position][query]
+  __shared__ __attribute__((aligned(16))) float s_sc[QP];              // this step's rescale factor of each query
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = blockIdx.x, kv = blockIdx.y;
+  const int c0 = c * kChunk;
+  const int jmax = min(c0 + kChunk - 1, a.p0 + a.T - 1);  // last position any row sees
+  if (c0 > jmax) return;
+  const int nq = a.T * G, nqt = (nq + 15) / 16;
+  const uint16_t* kbase = a.k + (int64_t)kv * a.S * D;
+  const uint16_t* vcol = a.v + (int64_t)kv * a.S * D + 64 * wave + lane;  // this lane's output dimension
+  // the queries of this KV head, row t's heads kv*G .. kv*G+G-1 as queries t*G ..
+  for (int i = threadIdx.x; i < QP * (D / 2); i += kAttnThreads) {
+    const int q = i / (D / 2), w = i % (D / 2);
+    s_q[q][w] = q < nq ? ((const uint32_t*)(a.q + ((int64_t)(q / G) * a.n_q + kv * G + q % G) * D))[w] : 0u;
+  }
+  // columns of queries past the call's: probability 0 and rescale 1 for good
+  for (int i = threadIdx.x; i < kMqStep * QP; i += kAttnThreads) {
+    const int j = i / QP, q = i % QP;
+    if (q >= nq) s_pt[j][q] = 0.f;
+  }
+  for (int q = threadIdx.x; q < QP; q += kAttnThreads)
+    if (q >= nq) s_sc[q] = 1.f;
+  float m_q[QPW], l_q[QPW], acc[QP];
+#pragma unroll
+  for (int j = 0; j < QPW; ++j) {
+    m_q[j] = -INFINITY;
+    l_q[j] = 0.f;
+  }
+#pragma unroll
+  for (int q = 0; q < QP; ++q) acc[q] = 0.f;
+  const int tl = lane & 15, kq = 8 * (lane >> 4);
+  // key rows of a step (B operand: position base + 16 wave + tl, dimensions
+  // kq + 32 ks .. + 7), requested one step ahead
+  u32x4 kb[D / 32];
+  auto load_k = [&](int base) {
+    const int pk = min(base + 16 * wave + tl, jmax);  // a visible row; masked below
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) kb[ks] = gload<u32x4>((const uint8_t*)(kbase + (int64_t)pk * D + 32 * ks + kq));
+  };
+  load_k(c0);
+  for (int base = c0; base <= jmax; base += kMqStep) {
+    // this step's values of the lane's dimension, requested first: they
+    // arrive while the scores and the softmax are computed
+    const int jl = min(kMqStep - 1, jmax - base);
+    uint16_t vr[kMqStep];
+#pragma unroll
+    for (int j = 0; j < kMqStep; ++j) vr[j] = gload<uint16_t>((const uint8_t*)(vcol + (int64_t)(base + min(j, jl)) * D));
+    mq_barrier();  // s_q written (first step); the previous step's LDS reads done
+    // (1) scores of positions base + 16 wave + tl for every query tile
+    {
+      at_f32x4 sc4[QP / 16];
+#pragma unroll
+      for (int qt = 0; qt < QP / 16; ++qt) {  // every tile: rows past the queries are zeros, masked below
+        sc4[qt] = at_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+          const u32x4 qa = *(const u32x4*)&s_q[16 * qt + tl][16 * ks + (kq >> 1)];
+          sc4[qt] = mfma_qk(qa, kb[ks], sc4[qt]);
+        }
+      }
+      if (base + kMqStep <= jmax) load_k(base + kMqStep);  // the next step's keys
+      const int pos = base + 16 * wave + tl;
+#pragma unroll
+      for (int qt = 0; qt < QP / 16; ++qt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int q = 16 * qt + 4 * (lane >> 4) + r;
+          const bool vis = q < nq && pos <= a.p0 + q / G;
+          s_s[q][16 * wave + tl] = vis ? sc4[qt][r] * a.scale : -INFINITY;
+        }
+      }
+    }
+    mq_barrier();
+    // (2) online softmax of queries wave, wave + 4, ... over the step
+#pragma unroll
+    for (int j = 0; j < QPW; ++j) {
+      const int q = wave + kAttnWaves * j;
+      if (q < nq) {
+        const float x = s_s[q][lane];
+        const float mn = fmaxf(m_q[j], wave_max(x));
+        float p = 0.f, sc = 1.f;
+        if (mn != -INFINITY) {
+          p = x == -INFINITY ? 0.f : expf(x - mn);
+          sc = m_q[j] == -INFINITY ? 0.f : expf(m_q[j] - mn);
+        }
+        const float sum = wave_sum(p);
+        l_q[j] = l_q[j] * sc + sum;
+        m_q[j] = mn;
+        s_pt[lane][q] = p;
+        if (lane == 0) s_sc[q] = sc;
+      }
+    }
+    mq_barrier();
+    // (3) weighted values: lane owns output dimension 64 wave + lane
+#pragma unroll
+    for (int q4 = 0; q4 < QP / 4; ++q4) {  // queries past the call's: rescale 1, probabilities 0
+      const float4 f = *(const float4*)&s_sc[4 * q4];
+      acc[4 * q4] *= f.x;
+      acc[4 * q4 + 1] *= f.y;
+      acc[4 * q4 + 2] *= f.z;
+      acc[4 * q4 + 3] *= f.w;
+    }
+    // positions past jl hold p = 0 for every query and a copy of row jl's value
+#pragma unroll
+    for (int j = 0; j < kMqStep; ++j) {
+      const float v = __uint_as_float((uint32_t)vr[j] << 16);
+      const float* prow = &s_pt[j][0];
+#pragma unroll
+      for (int q4 = 0; q4 < QP / 4; ++q4) {
+        const float4 pq = *(const float4*)&prow[4 * q4];
+        acc[4 * q4] = fmaf(pq.x, v, acc[4 * q4]);
+        acc[4 * q4 + 1] = fmaf(pq.y, v, acc[4 * q4 + 1]);
+        acc[4 * q4 + 2] = fmaf(pq.z, v, acc[4 * q4 + 2]);
+        acc[4 * q4 + 3] = fmaf(pq.w, v, acc[4 * q4 + 3]);
+      }
+    }
+  }
+  // the chunk's partials of the rows that see it
+#pragma unroll
+  for (int q = 0; q < QP; ++q) {
+    const int t = q / G;
+    if (q < nq && c0 <= a.p0 + t) {
+      float* dst = a.part + (((int64_t)c * a.T + t) * a.n_q + kv * G + q % G) * pstride<D>();
+      dst[4 + 64 * wave + lane] = acc[q];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < QPW; ++j) {
+    const int q = wave + kAttnWaves * j;
+    if (q < nq && lane == 0 && c0 <= a.p0 + q / G) {
+      float* dst = a.part + (((int64_t)c * a.T + q / G) * a.n_q + kv * G + q % G) * pstride<D>();
+      dst[0] = m_q[j];
+      dst[1] = l_q[j];
+    }
+  }
+}
+
 // One workgroup per (row, head, 64-element segment of the output). Wave w
 // takes the chunks w, w + kCombWaves, ... (kCombUnroll of them per round, all
 // loads of a round in flight) with a running maximum of its own; the waves'
@@ -446,7 +622,22 @@ extern "C" int32_t moe_gqa_decode(const moe_attn_shape_t* shape, int32_t T, int3
   switch (s.head_dim) {
     case 64: MOE_ATTN_D(64) break;
     case 128: MOE_ATTN_D(128) break;
-    default: MOE_ATTN_D(256) break;
+    default:
+      // the same per-query arithmetic in every instantiation: QP only
+      // sizes the registers and LDS for the call's T x g queries
+#define MOE_ATTN_MQ(GG)                                                                  \
+  case GG:                                                                               \
+    if (T * GG <= 16) attn_mq_kernel<GG, 16><<<g1, kAttnThreads, 0, st>>>(a);            \
+    else if (T * GG <= 32) attn_mq_kernel<GG, (GG >= 4 ? 32 : 16)><<<g1, kAttnThreads, 0, st>>>(a); \
+    else attn_mq_kernel<GG, (GG >= 8 ? 64 : 32)><<<g1, kAttnThreads, 0, st>>>(a);          \
+    break;
+      switch (a.g) {
+        MOE_ATTN_MQ(1) MOE_ATTN_MQ(2) MOE_ATTN_MQ(4)
+        default: MOE_ATTN_MQ(8)
+      }
+#undef MOE_ATTN_MQ
+      attn_combine_kernel<256><<<dim3(T * a.n_q, 256 / 64), 64 * kCombWaves, 0, st>>>(a);
+      break;
   }
 #undef MOE_ATTN_D
 #undef MOE_ATTN_G
