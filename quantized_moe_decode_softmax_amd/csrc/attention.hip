@@ -337,9 +337,10 @@ __device__ __forceinline__ void mq_barrier() { asm volatile("s_waitcnt lgkmcnt(0
 template <int G, int QP>
 __global__ void __launch_bounds__(kAttnThreads) attn_mq_kernel(AttnArgs a) {
   constexpr int D = 256;
-  constexpr int QPW = QP / kAttnWaves;  // softmax queries per wave
-  __shared__ __attribute__((aligned(16))) uint32_t s_q[QP][D / 2 + 4];  // bf16 pairs; rows padded by 16 bytes
-  __shared__ float s_s[QP][kMqStep + 1];                               // scaled, masked scores [query][position]
+  constexpr int QPW = QP / kAttnWaves;       // softmax queries per wave
+  constexpr int QT = (QP + 15) / 16 * 16;    // query rows of the score products (whole 16-row tiles)
+  __shared__ __attribute__((aligned(16))) uint32_t s_q[QT][D / 2 + 4];  // bf16 pairs; rows padded by 16 bytes
+  __shared__ float s_s[QT][kMqStep + 1];                               // scaled, masked scores [query][position]
   __shared__ __attribute__((aligned(16))) float s_pt[kMqStep][QP + 4];  // probabilities [position][query]
   __shared__ __attribute__((aligned(16))) float s_sc[QP];              // this step's rescale factor of each query
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -351,7 +352,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mq_kernel(AttnArgs a) {
   const uint16_t* kbase = a.k + (int64_t)kv * a.S * D;
   const uint16_t* vcol = a.v + (int64_t)kv * a.S * D + 64 * wave + lane;  // this lane's output dimension
   // the queries of this KV head, row t's heads kv*G .. kv*G+G-1 as queries t*G ..
-  for (int i = threadIdx.x; i < QP * (D / 2); i += kAttnThreads) {
+  for (int i = threadIdx.x; i < QT * (D / 2); i += kAttnThreads) {
     const int q = i / (D / 2), w = i % (D / 2);
     s_q[q][w] = q < nq ? ((const uint32_t*)(a.q + ((int64_t)(q / G) * a.n_q + kv * G + q % G) * D))[w] : 0u;
   }
@@ -390,9 +391,9 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mq_kernel(AttnArgs a) {
     mq_barrier();  // s_q written (first step); the previous step's LDS reads done
     // (1) scores of positions base + 16 wave + tl for every query tile
     {
-      at_f32x4 sc4[QP / 16];
+      at_f32x4 sc4[QT / 16];
 #pragma unroll
-      for (int qt = 0; qt < QP / 16; ++qt) {  // every tile: rows past the queries are zeros, masked below
+      for (int qt = 0; qt < QT / 16; ++qt) {  // every tile: rows past the queries are zeros, masked below
         sc4[qt] = at_f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) {
@@ -403,7 +404,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mq_kernel(AttnArgs a) {
       if (base + kMqStep <= jmax) load_k(base + kMqStep);  // the next step's keys
       const int pos = base + 16 * wave + tl;
 #pragma unroll
-      for (int qt = 0; qt < QP / 16; ++qt) {
+      for (int qt = 0; qt < QT / 16; ++qt) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int q = 16 * qt + 4 * (lane >> 4) + r;
@@ -625,17 +626,22 @@ extern "C" int32_t moe_gqa_decode(const moe_attn_shape_t* shape, int32_t T, int3
     default:
       // the same per-query arithmetic in every instantiation: QP only
       // sizes the registers and LDS for the call's T x g queries
-#define MOE_ATTN_MQ(GG)                                                                  \
-  case GG:                                                                               \
-    if (T * GG <= 16) attn_mq_kernel<GG, 16><<<g1, kAttnThreads, 0, st>>>(a);            \
-    else if (T * GG <= 32) attn_mq_kernel<GG, (GG >= 4 ? 32 : 16)><<<g1, kAttnThreads, 0, st>>>(a); \
-    else attn_mq_kernel<GG, (GG >= 8 ? 64 : 32)><<<g1, kAttnThreads, 0, st>>>(a);          \
-    break;
+// queries per instantiation: the smallest of 8, 16, 24, 32, 48, 64 that
+// holds the call's T x g (at most 8 g)
+#define MOE_ATTN_MQ_QP(GG, QQ) \
+  if (T * GG <= QQ) {          \
+    attn_mq_kernel<GG, QQ><<<g1, kAttnThreads, 0, st>>>(a); \
+    break;                     \
+  }
       switch (a.g) {
-        MOE_ATTN_MQ(1) MOE_ATTN_MQ(2) MOE_ATTN_MQ(4)
-        default: MOE_ATTN_MQ(8)
+        case 1: MOE_ATTN_MQ_QP(1, 8) break;
+        case 2: MOE_ATTN_MQ_QP(2, 8) MOE_ATTN_MQ_QP(2, 16) break;
+        case 4: MOE_ATTN_MQ_QP(4, 8) MOE_ATTN_MQ_QP(4, 16) MOE_ATTN_MQ_QP(4, 24) MOE_ATTN_MQ_QP(4, 32) break;
+        default:
+          MOE_ATTN_MQ_QP(8, 8) MOE_ATTN_MQ_QP(8, 16) MOE_ATTN_MQ_QP(8, 24) MOE_ATTN_MQ_QP(8, 32)
+          MOE_ATTN_MQ_QP(8, 48) MOE_ATTN_MQ_QP(8, 64) break;
       }
-#undef MOE_ATTN_MQ
+#undef MOE_ATTN_MQ_QP
       attn_combine_kernel<256><<<dim3(T * a.n_q, 256 / 64), 64 * kCombWaves, 0, st>>>(a);
       break;
   }
