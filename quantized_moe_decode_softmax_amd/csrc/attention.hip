@@ -335,7 +335,7 @@ __device__ __forceinline__ at_f32x4 mfma_qk(u32x4 a, u32x4 b, at_f32x4 c) {
 __device__ __forceinline__ void mq_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int G, int QP>
-__global__ void __launch_bounds__(kAttnThreads) attn_mq_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(kAttnThreads, 2) attn_mq_kernel(AttnArgs a) {
   constexpr int D = 256;
   constexpr int QPW = QP / kAttnWaves;       // softmax queries per wave
   constexpr int QT = (QP + 15) / 16 * 16;    // query rows of the score products (whole 16-row tiles)
@@ -385,9 +385,13 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mq_kernel(AttnArgs a) {
     // this step's values of the lane's dimension, requested first: they
     // arrive while the scores and the softmax are computed
     const int jl = min(kMqStep - 1, jmax - base);
-    uint16_t vr[kMqStep];
+    // (at 64 queries, whose registers would not leave two waves per SIMD
+    // otherwise, half of them now and the other half once the first half
+    // has been used)
+    constexpr int VN = QP >= 48 ? kMqStep / 2 : kMqStep;
+    uint16_t vr[VN];
 #pragma unroll
-    for (int j = 0; j < kMqStep; ++j) vr[j] = gload<uint16_t>((const uint8_t*)(vcol + (int64_t)(base + min(j, jl)) * D));
+    for (int j = 0; j < VN; ++j) vr[j] = gload<uint16_t>((const uint8_t*)(vcol + (int64_t)(base + min(j, jl)) * D));
     mq_barrier();  // s_q written (first step); the previous step's LDS reads done
     // (1) scores of positions base + 16 wave + tl for every query tile
     {
@@ -446,7 +450,12 @@ __global__ void __launch_bounds__(kAttnThreads) attn_mq_kernel(AttnArgs a) {
     // positions past jl hold p = 0 for every query and a copy of row jl's value
 #pragma unroll
     for (int j = 0; j < kMqStep; ++j) {
-      const float v = __uint_as_float((uint32_t)vr[j] << 16);
+      if (VN < kMqStep && j == VN) {
+#pragma unroll
+        for (int i = 0; i < VN; ++i)
+          vr[i] = gload<uint16_t>((const uint8_t*)(vcol + (int64_t)(base + min(VN + i, jl)) * D));
+      }
+      const float v = __uint_as_float((uint32_t)vr[j % VN] << 16);
       const float* prow = &s_pt[j][0];
 #pragma unroll
       for (int q4 = 0; q4 < QP / 4; ++q4) {
@@ -626,8 +635,9 @@ extern "C" int32_t moe_gqa_decode(const moe_attn_shape_t* shape, int32_t T, int3
     default:
       // the same per-query arithmetic in every instantiation: QP only
       // sizes the registers and LDS for the call's T x g queries
-// queries per instantiation: the smallest of 8, 16, 24, 32, 48, 64 that
-// holds the call's T x g (at most 8 g)
+// queries per instantiation: the smallest of 8, 16, 24, 32, 64 that holds
+// the call's T x g (at most 8 g; a 48-query instantiation measured slower
+// than the 64-query one)
 #define MOE_ATTN_MQ_QP(GG, QQ) \
   if (T * GG <= QQ) {          \
     attn_mq_kernel<GG, QQ><<<g1, kAttnThreads, 0, st>>>(a); \
@@ -639,7 +649,7 @@ extern "C" int32_t moe_gqa_decode(const moe_attn_shape_t* shape, int32_t T, int3
         case 4: MOE_ATTN_MQ_QP(4, 8) MOE_ATTN_MQ_QP(4, 16) MOE_ATTN_MQ_QP(4, 24) MOE_ATTN_MQ_QP(4, 32) break;
         default:
           MOE_ATTN_MQ_QP(8, 8) MOE_ATTN_MQ_QP(8, 16) MOE_ATTN_MQ_QP(8, 24) MOE_ATTN_MQ_QP(8, 32)
-          MOE_ATTN_MQ_QP(8, 48) MOE_ATTN_MQ_QP(8, 64) break;
+          MOE_ATTN_MQ_QP(8, 64) break;
       }
 #undef MOE_ATTN_MQ_QP
       attn_combine_kernel<256><<<dim3(T * a.n_q, 256 / 64), 64 * kCombWaves, 0, st>>>(a);
