@@ -9,8 +9,10 @@
 //                 token rows); workgroup 0 also writes the RMS factor
 //                 r_t = 1/sqrt(mean(h_t^2) + eps) and the shared expert's gate
 //                 sigmoid(r_t gvec . h_t). For T > 8 with an 8-bit router and
-//                 shared expert, route_mfma_kernel (mfma.h) does this on the
-//                 matrix cores and down_mfma_kernel the shared down projection.
+//                 shared expert, mfma_pack_kernel (mfma.h) writes r_t, the
+//                 gate and a packed copy of h, route_mfma_kernel does the rest
+//                 on the matrix cores and down_mfma_kernel the shared down
+//                 projection.
 //   select_kernel one workgroup: top-k of r_t W_r h_t for every row (ties to
 //                 the lower id, softmax renormalised over the k) and the
 //                 ascending list of experts used by any row, with row masks.
@@ -74,6 +76,8 @@ struct Ptrs {
   uint16_t* a_hi;
   uint16_t* a_lo;
   float* ysh;  // shared expert's down projection [T][H] from the matrix-core path, or nullptr
+  uint16_t* hp;  // matrix-core path: packed h (mfma.h)
+  uint16_t* ap;  // matrix-core path: packed shared activations, hi then lo
   // the layer block is table[li] (descriptor table in device memory) when
   // table is set, else `layer`
   const uint8_t* const* table;
@@ -333,12 +337,14 @@ __global__ void __launch_bounds__(256) route_kernel(Dims d, Ptrs p_, int n_rt) {
 // Routed experts for many token rows, one token row at a time per wave:
 // tasks are ordered (row t, slot, block of row pairs), a wave takes a run of
 // them, arranges x_t once per row and streams the gate/up rows of the row's
-// experts. An expert used by several rows is read once: the task of the
-// lowest row using it loads the block's rows and computes them for every row
-// in the expert's mask (arranging the other rows' inputs as it goes), and
-// the other rows' tasks for it do nothing. The arithmetic of a (row, pair) is
-// the one of swiglu_task whichever task computes it, so rows stay exact.
-template <int BITS, int CPL, int RP>
+// experts. With SHARE an expert used by several rows is read once: the task
+// of the lowest row using it loads the block's rows and computes them for
+// every row in the expert's mask (arranging the other rows' inputs as it
+// goes), and the other rows' tasks for it do nothing; without it every
+// (row, slot) task reads its expert itself, and the kernel carries none of
+// that code. The arithmetic of a (row, pair) is the one of swiglu_task
+// whichever task computes it, so rows stay exact.
+template <int BITS, int CPL, int RP, bool SHARE>
 __device__ __forceinline__ void swiglu_rows(const Dims& d, const Ptrs& p, int task0, int task1, int tps, int li,
                                             int lpr, int sr, int rpw) {
   constexpr int R = 2 * RP;
@@ -358,8 +364,8 @@ __device__ __forceinline__ void swiglu_rows(const Dims& d, const Ptrs& p, int ta
       }
     }
     const int e = p.ids[t * d.k + slot];
-    const uint32_t emask = p.tmask[t * d.k + slot];  // loaded beside the id, not after it
-    if ((int)__builtin_ctz(emask) != t) continue;  // a lower row's task computes this expert block
+    const uint32_t emask = SHARE ? p.tmask[t * d.k + slot] : 1u << t;  // loaded beside the id, not after it
+    if (SHARE && (int)__builtin_ctz(emask) != t) continue;  // a lower row's task computes this expert block
     const uint8_t* gate = p.layer + d.off_e0 + (int64_t)e * d.e_stride;
     const uint8_t* up = gate + d.off_e_up;
     const uint32_t* gsb = (const uint32_t*)(gate + cb);
@@ -394,7 +400,7 @@ __device__ __forceinline__ void swiglu_rows(const Dims& d, const Ptrs& p, int ta
       if (pairs[q] >= 0 && li == lpr - 1) store_a(d, p, t, slot, pairs[q], silu_mul(g, v));
     }
     // the later rows using this expert, from the same loaded rows
-    for (uint32_t rest = emask & (emask - 1u); rest; rest &= rest - 1u) {
+    if constexpr (SHARE) for (uint32_t rest = emask & (emask - 1u); rest; rest &= rest - 1u) {
       const int t2 = __builtin_ctz(rest);
       int slot2 = 0;
       for (int i = 0; i < d.k; ++i)
@@ -420,7 +426,9 @@ __device__ __forceinline__ void swiglu_rows(const Dims& d, const Ptrs& p, int ta
 // costs no time, at T = 32 (397B-A17B low-bit shape, 113 distinct experts of
 // 128 selections per layer) it took the kernel from 171 to 259 us per layer
 // against 12% fewer bytes, so there each row reads its expert itself (the
-// down projections still read each distinct expert once).
+// down projections still read each distinct expert once). Calls above it
+// run a kernel compiled without the sharing code (the code alone, never
+// executed, made the T = 32 kernel about 8% slower).
 constexpr int kShareMaxT = 8;
 
 // ---------------------------------------------------------- select kernel
@@ -506,7 +514,7 @@ __global__ void __launch_bounds__(256, 2) expert_kernel(Dims d, Ptrs p_, int tas
 }
 
 // grid: waves of tpw consecutive (row, slot, block) tasks, tps blocks per slot
-template <int CPL>
+template <int CPL, bool SHARE>
 __global__ void __launch_bounds__(256, 2) expert_rows_kernel(Dims d, Ptrs p_, int tps, int tpw) {
   const Ptrs p = with_layer(p_);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -515,7 +523,7 @@ __global__ void __launch_bounds__(256, 2) expert_rows_kernel(Dims d, Ptrs p_, in
   const int n_tasks = d.T * d.k * tps;
   const int task0 = (blockIdx.x * 4 + wave) * tpw;
   const int task1 = task0 + tpw < n_tasks ? task0 + tpw : n_tasks;
-  MOE_BITS_CASES(d.ebits, B, swiglu_rows<B, CPL, RP>(d, p, task0, task1, tps, li, lpr, sr, rpw));
+  MOE_BITS_CASES(d.ebits, B, swiglu_rows<B, CPL, RP, SHARE>(d, p, task0, task1, tps, li, lpr, sr, rpw));
 }
 
 // ------------------------------------------------------------ down kernel
@@ -720,9 +728,9 @@ LayerPlan make_plan(const moe_shape_t& s, const moe_layer_layout_t& L, int T, in
   P.d_threads = 64 * nw;
   P.mfma = T >= kMfmaMinT && s.router_bits == 8 && s.shared_bits == 8 && !(flags & MOE_PATH_NO_MFMA);
   P.m_nt = T > 16 ? 2 : 1;
-  // groups in flight per wave, bounded by registers: 8 only with one token tile
+  // groups in flight per wave, bounded by registers (the down projection has
+  // two input parts)
   P.m_ng_route = mfma_groups_per_load(s.hidden / kGroup);
-  if (P.m_nt == 2 && P.m_ng_route > 4) P.m_ng_route = 4;
   P.m_ng_down = mfma_groups_per_load(s.shared_inter / kGroup);
   if (P.m_ng_down > 4) P.m_ng_down = 4;
   P.m_rt = (s.n_experts + 15) / 16;
@@ -740,19 +748,19 @@ template <int CPL>
 void launch_expert(const LayerPlan& P, const Ptrs& p, hipStream_t st) {
   select_kernel<<<1, 1024, 0, st>>>(P.d, p);
   if (P.rows_grid > 0)
-    expert_rows_kernel<CPL><<<P.rows_grid, 256, 0, st>>>(P.d, p, P.tpu, P.rows_tpw);
+    // at four chunks per lane the sharing code spills registers
+    if (CPL < 4 && P.d.T <= kShareMaxT)
+      expert_rows_kernel<CPL, CPL < 4><<<P.rows_grid, 256, 0, st>>>(P.d, p, P.tpu, P.rows_tpw);
+    else
+      expert_rows_kernel<CPL, false><<<P.rows_grid, 256, 0, st>>>(P.d, p, P.tpu, P.rows_tpw);
   else
     expert_kernel<CPL><<<P.g_grid, 256, 0, st>>>(P.d, p, P.tpu);
 }
 template <int NT>
 void launch_mfma(const LayerPlan& P, const Ptrs& p, hipStream_t st) {
+  mfma_pack_kernel<<<16 * NT, 256, 0, st>>>(P.d, p);
   switch (P.m_ng_route) {
-    case 8:
-      if constexpr (NT == 1) {
-        route_mfma_kernel<1, 8><<<P.m_rt + P.m_pt, kMfmaThreads, 0, st>>>(P.d, p, P.m_rt);
-        break;
-      }
-      [[fallthrough]];
+    case 8: route_mfma_kernel<NT, 8><<<P.m_rt + P.m_pt, kMfmaThreads, 0, st>>>(P.d, p, P.m_rt); break;
     case 4: route_mfma_kernel<NT, 4><<<P.m_rt + P.m_pt, kMfmaThreads, 0, st>>>(P.d, p, P.m_rt); break;
     default: route_mfma_kernel<NT, 2><<<P.m_rt + P.m_pt, kMfmaThreads, 0, st>>>(P.d, p, P.m_rt); break;
   }
@@ -796,6 +804,8 @@ int32_t launch_layer(const LayerPlan& P, const WsMap& m, uint8_t* ws, const uint
   p.a_hi = (uint16_t*)(ws + m.a_hi);
   p.a_lo = (uint16_t*)(ws + m.a_lo);
   p.ysh = nullptr;
+  p.hp = (uint16_t*)(ws + m.hpack);
+  p.ap = (uint16_t*)(ws + m.apack);
   if (P.mfma) {
     p.ysh = (float*)(ws + m.ysh);
     if (P.m_nt == 2) launch_mfma<2>(P, p, st);

@@ -115,7 +115,8 @@ __host__ __device__ __forceinline__ int chunks_per_lane(int k) {
 }
 
 __device__ __forceinline__ void load64B(const void* p, uint32_t (&w)[16]) {
-  const u32x4* q = (const u32x4*)p;
+  // global memory (address space 1): a global_load, not a flat one
+  const __attribute__((address_space(1))) u32x4* q = (const __attribute__((address_space(1))) u32x4*)p;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const u32x4 v = q[i];

@@ -62,6 +62,8 @@ struct WsMap {
   int64_t a_lo;         // bf16  [T][k+1][Imax]  low part: a = hi + lo to 16 significant bits
   int64_t hbuf;         // bf16  [2][T][H] ping-pong for stacks
   int64_t ysh;          // float [T][H]  shared expert's down projection (matrix-core path)
+  int64_t hpack;        // bf16 [T16][H] packed h (matrix-core path; T16 = T rounded up to 16)
+  int64_t apack;        // bf16 [2][T16][Is] packed shared activations, hi then lo (matrix-core path)
   // one-row streaming stack kernel (stack1.hip): exchange buffers of 64-bit
   // words = 32-bit payload | epoch << 32, each in n_copy copies (stride *_cs
   // words) that writers all store and workgroup w reads copy w % n_copy

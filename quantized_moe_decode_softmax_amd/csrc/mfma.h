@@ -17,15 +17,25 @@
 // are applied on the vector unit. With x = h (bf16, the layer input) the RMS
 // factor r_t multiplies y afterwards (RMSNorm has weight 1); the down
 // projection's input a is the activation split a = hi + lo (two bf16 parts),
-// each part its own product. sum_j h^2 (for r_t) is the diagonal of the
-// 16 x 16 Gram product h h^T of each token tile, also on the matrix cores.
+// each part its own product.
 //
 // Operand layout of v_mfma_f32_16x16x32_bf16 (wave64): lane l supplies, for
-// A (16 x 32), row l % 16 and the 8 consecutive k = 8 (l / 16) .. + 7; for
-// B (32 x 16) column l % 16 and the same k; it receives D[4 (l / 16) + i]
-// [l % 16], i = 0..3. Token rows are A's rows (16 per tile, NT tiles), weight
-// rows B's columns (16 per workgroup), so each lane converts 8 codes per
-// instruction pair and keeps one output row's scale and bias.
+// A (16 x 32), row l % 16 and the 8 k-slots 8 (l / 16) .. + 7; for B (32 x 16)
+// column l % 16 and the same slots; it receives D[4 (l / 16) + i][l % 16],
+// i = 0..3. Token rows are A's rows (16 per tile, NT tiles), weight rows B's
+// columns (16 per workgroup). A sum over k does not depend on which k sits in
+// which slot as long as A and B agree, so the two products of group g give
+// lane quadrant q the inputs 64 g + 16 q + 8 c .. + 7 (c = 0, 1): each lane
+// loads its weight row's 16 codes of the group in one 16-byte load (a full
+// 64-byte group per row and instruction).
+//
+// Token-row operands are read from a packed copy (mfma_pack_kernel for h, the
+// shared expert's SwiGLU for a) in which the A operand of one product, tile tt,
+// group g, half c, is 1 KB in lane order: element e of lane l = 16 q + r is
+// x[16 tt + r][64 g + 16 q + 8 c + e]. A wave's load of it is one contiguous
+// kilobyte; loaded from the row-major [T][K] array the same operand is 16
+// rows of 64 bytes a whole row apart, which measured 5 to 6 us slower per
+// call at T = 32 and H = 4096 (every workgroup reads all of h).
 //
 // Work split: one workgroup of 8 waves per 16 weight rows; the waves split
 // the groups of K and their partial sums are added in wave order in LDS
@@ -69,97 +79,132 @@ __device__ __forceinline__ mf_u32x4 codes8_bf16(mf_u32x2 q) {
   return r;
 }
 
-// A operand rows: NX parts (1: x = h; 2: x = hi + lo), token row t of part n
-// at a[n] + t * stride (bf16 elements). Rows t >= T read row T - 1 instead:
-// output row t of a product depends on A's row t only, and rows t >= T are
-// never stored.
-template <int NX>
-struct MfA {
-  const uint16_t* a[NX];
-  int64_t stride;
-  int T;
-};
+// Element index of x[t][k] in the packed copy of a [16 NT][K] operand
+// (G = K / 64 groups): block (t / 16, k / 64, half), lane 16 q + t % 16.
+__device__ __forceinline__ int64_t packed_index(int t, int k, int G) {
+  const int g = k >> 6, w = k & 63, q = w >> 4, c = (w >> 3) & 1, e = w & 7;
+  return ((((int64_t)(t >> 4) * G + g) * 2 + c) * 64 + 16 * q + (t & 15)) * 8 + e;
+}
+
+// Packed copy of h for the matrix-core kernels, and the per-row statistics:
+// r_t = 1 / sqrt(mean(h_t^2) + eps) and the shared expert's gate
+// sigmoid(r_t gvec . h_t). One workgroup per token row of 16 NT (rows t >= T
+// are written as zeros); thread j takes 16 consecutive inputs per pass (one
+// lane quadrant of a group: both halves), so the row is read contiguously.
+// The sums are fp32 in a fixed order (thread, then wave tree, then waves).
+__global__ void __launch_bounds__(256) mfma_pack_kernel(Dims d, Ptrs p_) {
+  const Ptrs p = with_layer(p_);
+  __shared__ float s_part[2][4];
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = d.H >> 6, nq = d.H >> 4;
+  const bool live = t < d.T;
+  const uint16_t* gvec = (const uint16_t*)(p.layer + d.off_gatevec);
+  float ss = 0.f, gd = 0.f;
+  for (int j = tid; j < nq; j += 256) {
+    mf_u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
+    if (live) {
+      x0 = gload<mf_u32x4>((const uint8_t*)(p.h_in + (int64_t)t * d.H + 16 * j));
+      x1 = gload<mf_u32x4>((const uint8_t*)(p.h_in + (int64_t)t * d.H + 16 * j + 8));
+      const mf_u32x4 g0 = gload<mf_u32x4>((const uint8_t*)(gvec + 16 * j));
+      const mf_u32x4 g1 = gload<mf_u32x4>((const uint8_t*)(gvec + 16 * j + 8));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a0 = bf16_lo_to_f32(x0[i]), a1 = bf16_hi_to_f32(x0[i]);
+        const float b0 = bf16_lo_to_f32(x1[i]), b1 = bf16_hi_to_f32(x1[i]);
+        ss = fmaf(a0, a0, ss);
+        ss = fmaf(a1, a1, ss);
+        ss = fmaf(b0, b0, ss);
+        ss = fmaf(b1, b1, ss);
+        gd = fmaf(a0, bf16_lo_to_f32(g0[i]), gd);
+        gd = fmaf(a1, bf16_hi_to_f32(g0[i]), gd);
+        gd = fmaf(b0, bf16_lo_to_f32(g1[i]), gd);
+        gd = fmaf(b1, bf16_hi_to_f32(g1[i]), gd);
+      }
+    }
+    const int k = 16 * j;
+    *(mf_u32x4*)(p.hp + packed_index(t, k, G)) = x0;
+    *(mf_u32x4*)(p.hp + packed_index(t, k + 8, G)) = x1;
+  }
+  if (!live) return;
+  ss = wave_sum(ss);
+  gd = wave_sum(gd);
+  if (lane == 0) {
+    s_part[0][wave] = ss;
+    s_part[1][wave] = gd;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const float sq = (s_part[0][0] + s_part[0][1]) + (s_part[0][2] + s_part[0][3]);
+    const float g = (s_part[1][0] + s_part[1][1]) + (s_part[1][2] + s_part[1][3]);
+    const float r = rms_factor(sq, d.H, d.eps);
+    p.rinv[t] = r;
+    p.sg[t] = 1.0f / (1.0f + expf(-(r * g)));
+  }
+}
 
 // Partial sums of one wave over groups [g0, g1) of the 16 weight rows; the
 // lane's weight row starts at row (codes) and sbrow (scale|bias words); a
-// lane whose output column is not stored passes any valid row. acc[tt]: y of
-// token tile tt; ss[tt]: Gram product of part 0 (SS); gd[tt]: x . gvec (GD).
-// Every load is unconditional (clamped addresses), so the NG groups' loads
-// are all in flight before the first product.
-template <int NT, int NX, int NG, bool SS, bool GD>
-__device__ __forceinline__ void mfma_groups(const MfA<NX>& A, const uint8_t* row, const uint32_t* sbrow, int g0,
-                                            int g1, const uint16_t* gvec, mf_f32x4 (&acc)[NT], mf_f32x4 (&ss)[NT],
-                                            mf_f32x4 (&gd)[NT]) {
-  const int lane = threadIdx.x & 63, tl = lane & 15, kq = 8 * (lane >> 4);
+// lane whose output column is not stored passes any valid row. x[n]: packed
+// token-row operand of part n (G groups per row). acc[tt]: y of token tile tt.
+// Every load is unconditional (clamped group), so the NG groups' loads are
+// all in flight before the first product.
+template <int NT, int NX, int NG>
+__device__ __forceinline__ void mfma_groups(const uint16_t* const (&x)[NX], int G, const uint8_t* row,
+                                            const uint32_t* sbrow, int g0, int g1, mf_f32x4 (&acc)[NT]) {
+  const int lane = threadIdx.x & 63, q = lane >> 4;
   const mf_u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-  const uint16_t* arow[NX][NT];
-#pragma unroll
-  for (int n = 0; n < NX; ++n)
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
-      const int t = 16 * tt + tl;
-      arow[n][tt] = A.a[n] + (t < A.T ? t : A.T - 1) * A.stride;
-    }
   for (int gb = g0; gb < g1; gb += NG) {
     mf_u32x4 xa[NG][NX][NT][2];
-    mf_u32x2 q[NG][2];
-    mf_u32x4 gv[NG][2];
+    mf_u32x4 bq[NG];
     uint32_t sbw[NG];
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
       const int g = gb + j < g1 ? gb + j : g1 - 1;
+      bq[j] = gload<mf_u32x4>(row + 64 * g + 16 * q);
+      sbw[j] = gload<uint32_t>((const uint8_t*)(sbrow + g));
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int k = 64 * g + 32 * ks + kq;
+      for (int n = 0; n < NX; ++n)
 #pragma unroll
-        for (int n = 0; n < NX; ++n)
+        for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-          for (int tt = 0; tt < NT; ++tt) xa[j][n][tt][ks] = *(const mf_u32x4*)(arow[n][tt] + k);
-        q[j][ks] = *(const mf_u32x2*)(row + k);
-        if constexpr (GD) gv[j][ks] = *(const mf_u32x4*)(gvec + k);
-      }
-      sbw[j] = sbrow[g];
+          for (int c = 0; c < 2; ++c)
+            xa[j][n][tt][c] =
+                gload<mf_u32x4>((const uint8_t*)(x[n] + ((((int64_t)tt * G + g) * 2 + c) * 64 + lane) * 8));
     }
+    // the scheduler would otherwise sink each load to its first use, a round
+    // trip per product
+    __builtin_amdgcn_sched_barrier(0);
     // every group of the chunk is computed (no branch keeps the loads above
     // from being hoisted); a group past g1 is weighted by 0
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
       const float okf = gb + j < g1 ? 1.f : 0.f;
-      mf_f32x4 D[NT], X[NT], S2[NT], G2[NT];
+      mf_f32x4 D[NT], X[NT];
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt) D[tt] = X[tt] = S2[tt] = G2[tt] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int tt = 0; tt < NT; ++tt) D[tt] = X[tt] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const mf_u32x4 b = codes8_bf16(q[j][ks]);
+      for (int c = 0; c < 2; ++c) {
+        const mf_u32x4 b = codes8_bf16(c ? mf_u32x2{bq[j].z, bq[j].w} : mf_u32x2{bq[j].x, bq[j].y});
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
+        for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
           for (int n = 0; n < NX; ++n) {
-            D[tt] = mfma_bf16(xa[j][n][tt][ks], b, D[tt]);
-            X[tt] = mfma_bf16(xa[j][n][tt][ks], ones, X[tt]);
+            D[tt] = mfma_bf16(xa[j][n][tt][c], b, D[tt]);
+            X[tt] = mfma_bf16(xa[j][n][tt][c], ones, X[tt]);
           }
-          if constexpr (SS) S2[tt] = mfma_bf16(xa[j][0][tt][ks], xa[j][0][tt][ks], S2[tt]);
-          if constexpr (GD) G2[tt] = mfma_bf16(xa[j][0][tt][ks], gv[j][ks], G2[tt]);
-        }
       }
       const float s = okf * bf16_lo_to_f32(sbw[j]), bb = okf * bf16_hi_to_f32(sbw[j]);
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[tt][i] = fmaf(s, D[tt][i], fmaf(bb, X[tt][i], acc[tt][i]));
-          if constexpr (SS) ss[tt][i] = fmaf(okf, S2[tt][i], ss[tt][i]);
-          if constexpr (GD) gd[tt][i] = fmaf(okf, G2[tt][i], gd[tt][i]);
-        }
+        for (int i = 0; i < 4; ++i) acc[tt][i] = fmaf(s, D[tt][i], fmaf(bb, X[tt][i], acc[tt][i]));
     }
   }
 }
 
 // LDS for the cross-wave sums: [wave][value][lane]
 struct MfmaLds {
-  float red[kMfmaWaves][3 * 2 * 4][64];
-  float r[32];
-  float gd[32];
+  float red[kMfmaWaves][2 * 4][64];
 };
 
 // Adds the waves' values v[0..nv) (per lane) in wave order; the totals land
@@ -182,8 +227,9 @@ __device__ __forceinline__ void mfma_reduce(MfmaLds& L, float (&v)[NV]) {
 
 // Router logits (before the RMS factor) and shared-expert activations of all
 // T rows. Workgroups [0, n_rt): 16 router rows each; [n_rt, ..): 8 shared
-// pairs each (gate rows as columns 0..7, up rows as 8..15). The first pair
-// workgroup also writes r_t and the shared gate sigmoid(r_t gvec . h_t).
+// pairs each (gate rows as columns 0..7, up rows as 8..15), whose activations
+// go to the packed copy the shared down projection reads (rows t >= T: 0).
+// r_t comes from mfma_pack_kernel, launched before.
 template <int NT, int NG>
 __global__ void __launch_bounds__(kMfmaThreads) route_mfma_kernel(Dims d, Ptrs p_, int n_rt) {
   const Ptrs p = with_layer(p_);
@@ -210,49 +256,30 @@ __global__ void __launch_bounds__(kMfmaThreads) route_mfma_kernel(Dims d, Ptrs p
     row = base + ic * rb;
     sbrow = (const uint32_t*)(base + matrix_codes_bytes(8, d.Is, d.H)) + (int64_t)ic * G;
   }
-  const bool stats = (int)blockIdx.x == n_rt;
-  MfA<1> A;
-  A.a[0] = p.h_in;
-  A.stride = d.H;
-  A.T = d.T;
-  mf_f32x4 acc[NT], ss[NT], gd[NT];
-#pragma unroll
-  for (int tt = 0; tt < NT; ++tt) acc[tt] = ss[tt] = gd[tt] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
-  const uint16_t* gvec = (const uint16_t*)(p.layer + d.off_gatevec);
-  if (g0 < g1) {
-    if (router)
-      mfma_groups<NT, 1, NG, false, false>(A, row, sbrow, g0, g1, gvec, acc, ss, gd);
-    else if (stats)
-      mfma_groups<NT, 1, NG, true, true>(A, row, sbrow, g0, g1, gvec, acc, ss, gd);
-    else
-      mfma_groups<NT, 1, NG, true, false>(A, row, sbrow, g0, g1, gvec, acc, ss, gd);
-  }
-  float v[3 * NT * 4];
+  const uint16_t* const x[1] = {p.hp};
+  // the RMS factors of the lane's output rows, requested before the products
+  // so that the epilogue does not wait for them
+  float rt[NT][4];
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      v[4 * tt + c] = acc[tt][c];
-      v[4 * NT + 4 * tt + c] = ss[tt][c];
-      v[8 * NT + 4 * tt + c] = gd[tt][c];
+      const int t = 16 * tt + 4 * (lane >> 4) + c;
+      rt[tt][c] = !router && wave == 0 && t < d.T ? p.rinv[t] : 0.f;
     }
+  mf_f32x4 acc[NT];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) acc[tt] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
+  if (g0 < g1) mfma_groups<NT, 1, NG>(x, G, row, sbrow, g0, g1, acc);
+  float v[4 * NT];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[4 * tt + c] = acc[tt][c];
   mfma_reduce(L, v);
-  // lane holds rows t = 16 tt + 4 (lane / 16) + c of column tl
-  if (wave == 0 && !router) {
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int tr = 4 * (lane >> 4) + c;
-        if (tr == tl) {  // Gram diagonal
-          const int t = 16 * tt + tr;
-          L.r[t] = rms_factor(v[4 * NT + 4 * tt + c], d.H, d.eps);
-          L.gd[t] = v[8 * NT + 4 * tt + c];
-        }
-      }
-  }
-  __syncthreads();
   if (wave != 0) return;
+  // lane holds rows t = 16 tt + 4 (lane / 16) + c of column tl
+  const int Gi = d.Is >> 6;
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
@@ -262,22 +289,22 @@ __global__ void __launch_bounds__(kMfmaThreads) route_mfma_kernel(Dims d, Ptrs p
       if (router) {
         if (t < d.T && e >= 0 && e < d.E) p.raw[(int64_t)t * d.E + e] = y;
       } else {
-        const float r = L.r[t];
-        const float yv = y * r;
+        const float yv = y * rt[tt][c];
         const float partner = __shfl_xor(yv, 8);  // up row of the same pair
-        if (t < d.T && tl < 8 && i < d.Is) store_a(d, p, t, d.k, i, silu_mul(yv, partner));
+        if (tl < 8 && i < d.Is) {
+          const float a = silu_mul(yv, partner);
+          const uint32_t hb = __float_as_uint(a) & 0xFFFF0000u;
+          const int64_t idx = packed_index(t, i, Gi);
+          p.ap[idx] = (uint16_t)(hb >> 16);
+          p.ap[(int64_t)16 * NT * d.Is + idx] = (uint16_t)f32_to_bf16_rne(a - __uint_as_float(hb));
+        }
       }
     }
-  if (stats && lane < d.T) {
-    const float r = L.r[lane];
-    p.rinv[lane] = r;
-    p.sg[lane] = 1.0f / (1.0f + expf(-(r * L.gd[lane])));
-  }
 }
 
 // Shared expert's down projection y_s[t][j] = W_d a_s[t] (fp32, before the
-// gate) for 16 output rows per workgroup; a_s = hi + lo from the activation
-// slot k.
+// gate) for 16 output rows per workgroup; a_s = hi + lo from the packed copy
+// the route kernel wrote.
 template <int NT, int NG>
 __global__ void __launch_bounds__(kMfmaThreads) down_mfma_kernel(Dims d, Ptrs p_) {
   const Ptrs p = with_layer(p_);
@@ -291,15 +318,11 @@ __global__ void __launch_bounds__(kMfmaThreads) down_mfma_kernel(Dims d, Ptrs p_
   const uint8_t* base = p.layer + d.off_shared + d.off_shared_down;
   const uint8_t* row = base + (int64_t)jc * d.Is;
   const uint32_t* sbrow = (const uint32_t*)(base + matrix_codes_bytes(8, d.H, d.Is)) + (int64_t)jc * G;
-  MfA<2> A;
-  A.a[0] = p.a_hi + (int64_t)d.k * d.imax;
-  A.a[1] = p.a_lo + (int64_t)d.k * d.imax;
-  A.stride = (int64_t)(d.k + 1) * d.imax;
-  A.T = d.T;
-  mf_f32x4 acc[NT], ss[NT], gd[NT];
+  const uint16_t* const x[2] = {p.ap, p.ap + (int64_t)16 * NT * d.Is};
+  mf_f32x4 acc[NT];
 #pragma unroll
-  for (int tt = 0; tt < NT; ++tt) acc[tt] = ss[tt] = gd[tt] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
-  if (g0 < g1) mfma_groups<NT, 2, NG, false, false>(A, row, sbrow, g0, g1, nullptr, acc, ss, gd);
+  for (int tt = 0; tt < NT; ++tt) acc[tt] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
+  if (g0 < g1) mfma_groups<NT, 2, NG>(x, G, row, sbrow, g0, g1, acc);
   float v[4 * NT];
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt)

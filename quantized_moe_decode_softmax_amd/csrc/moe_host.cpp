@@ -96,6 +96,9 @@ WsMap ws_map(const moe_shape_t& s, int T) {
   m.a_lo = take((int64_t)T * (k + 1) * imax * 2);
   m.hbuf = take((int64_t)2 * T * s.hidden * 2);
   m.ysh = take((int64_t)T * s.hidden * 4);
+  const int64_t t16 = ((int64_t)T + 15) / 16 * 16;
+  m.hpack = take(t16 * s.hidden * 2);
+  m.apack = take(2 * t16 * s.shared_inter * 2);
   m.n_copy = kExchangeCopies;
   m.xh_cs = align_up(s.hidden / 2, 512);
   m.xl_cs = align_up(s.n_experts, 512);
