@@ -58,7 +58,7 @@ KERNEL_SOURCES = ["stack1.hip", "gemv.h", "device_common.h", "internal.h"]  # th
 # 256 MiB device copy measured the same way. Keyed by workload; valid only
 # for the kernel sources whose hash is stored with it.
 TRAFFIC = {
-    "a3b": {"src_hash": "1e6ab73fe2c8e598", "fetch_bytes": 997_662_964, "write_bytes": 13_120_750},
+    "a3b": {"src_hash": "da5317949b5defb0", "fetch_bytes": 997_608_460, "write_bytes": 13_120_410},
 }
 
 
@@ -82,7 +82,7 @@ def kernel_path(w) -> str:
     if w.T == 1:
         return f"stack1_kernel: all {w.n_layers} layers in one launch (timed with its clear kernel)"
     if w.T > 8 and w.router_bits == 8 and w.shared_bits == 8:
-        return (f"per-layer kernels: route_mfma, down_mfma, select, expert, down per layer ({w.n_layers} "
+        return (f"per-layer kernels: mfma_pack, route_mfma, down_mfma, select, expert, down per layer ({w.n_layers} "
                 f"layers, timed together)")
     return f"per-layer kernels: route, select, expert, down per layer ({w.n_layers} layers, timed together)"
 
