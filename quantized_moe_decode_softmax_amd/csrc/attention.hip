@@ -26,7 +26,8 @@
 // 2 KV heads, head dimension 256; bf16 KV cache ("Hardware"). Scores are the
 // bf16 products of q and k accumulated in fp32 (v_dot2c_f32_bf16, or the
 // matrix cores at head dimension 256), scaled by 1/sqrt(d); probabilities and
-// the output are fp32.
+// the output are fp32 (at head dimension 256 the probabilities enter the
+// weighted sum of values as two bf16 parts, exact to 2^-18 relative).
 #include <cmath>
 
 #include "gemv.h"
@@ -314,14 +315,19 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a) 
 // scores of positions [16w, 16w + 16) of the step for every query tile and
 // writes them, scaled and masked, to LDS; wave w then runs the online
 // softmax of queries w, w + 4, ... over the 64 positions (wave-wide max and
-// sum in a fixed tree) and writes their probabilities [position][query] and
-// rescale factors; finally each lane of the workgroup owns one of the 256
-// output dimensions and accumulates p * v over the step's positions for
-// every query (each V row read once, 128 bytes per wave). A query's result
-// depends only on its own row's data: steps past a row's position add
-// exactly nothing (p = 0, rescale 1), so a verify row equals a one-row call.
+// sum in a fixed tree) and writes their probabilities, split p = hi + lo into
+// two bf16 parts (hi the nearest bf16, lo the nearest to the rest: 2^-18 of
+// p at most is lost), as the A operand of a second product, and the rescale
+// factors; finally wave w rescales its accumulators and adds
+// P_hi V + P_lo V for output dimensions [64w, 64w + 64) on the matrix cores
+// (V as the B operand, gathered with 16-bit loads two positions to a
+// register; each V element read once). A query's result depends only on its
+// own row's data, and each instantiation computes a row the same way: steps
+// past a row's position add exactly nothing (p = 0, rescale 1), so a verify
+// row equals a one-row call.
 typedef __bf16 at_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float at_f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t at_u16x2 __attribute__((ext_vector_type(2)));
 constexpr int kMqStep = 64;  // positions per step (16 per wave)
 
 __device__ __forceinline__ at_f32x4 mfma_qk(u32x4 a, u32x4 b, at_f32x4 c) {
@@ -338,11 +344,17 @@ template <int G, int QP>
 __global__ void __launch_bounds__(kAttnThreads, 2) attn_mq_kernel(AttnArgs a) {
   constexpr int D = 256;
   constexpr int QPW = QP / kAttnWaves;       // softmax queries per wave
-  constexpr int QT = (QP + 15) / 16 * 16;    // query rows of the score products (whole 16-row tiles)
+  constexpr int QT = (QP + 15) / 16 * 16;    // query rows of the products (whole 16-row tiles)
+  constexpr int NQT = QT / 16;
   __shared__ __attribute__((aligned(16))) uint32_t s_q[QT][D / 2 + 4];  // bf16 pairs; rows padded by 16 bytes
   __shared__ float s_s[QT][kMqStep + 1];                               // scaled, masked scores [query][position]
-  __shared__ __attribute__((aligned(16))) float s_pt[kMqStep][QP + 4];  // probabilities [position][query]
-  __shared__ __attribute__((aligned(16))) float s_sc[QP];              // this step's rescale factor of each query
+  // probabilities as the A operand of the weighted-value product: per query
+  // tile, half step kb (32 positions) and part (p = hi + lo, two bf16), 64
+  // lanes x 8 bf16: lane 16 g + r holds query 16 qt + r, positions
+  // 32 kb + 8 g .. + 7
+  __shared__ __attribute__((aligned(16))) uint16_t s_pa[NQT][2][2][64 * 8];
+  __shared__ __attribute__((aligned(16))) float s_sc[QT];              // this step's rescale factor of each query
+  __shared__ float s_m[QT], s_l[QT];                                   // running maximum and sum of each query
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = blockIdx.x, kv = blockIdx.y;
   const int c0 = c * kChunk;
@@ -350,27 +362,31 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_mq_kernel(AttnArgs a) {
   if (c0 > jmax) return;
   const int nq = a.T * G, nqt = (nq + 15) / 16;
   const uint16_t* kbase = a.k + (int64_t)kv * a.S * D;
-  const uint16_t* vcol = a.v + (int64_t)kv * a.S * D + 64 * wave + lane;  // this lane's output dimension
+  const uint16_t* vbase = a.v + (int64_t)kv * a.S * D;
   // the queries of this KV head, row t's heads kv*G .. kv*G+G-1 as queries t*G ..
   for (int i = threadIdx.x; i < QT * (D / 2); i += kAttnThreads) {
     const int q = i / (D / 2), w = i % (D / 2);
     s_q[q][w] = q < nq ? ((const uint32_t*)(a.q + ((int64_t)(q / G) * a.n_q + kv * G + q % G) * D))[w] : 0u;
   }
-  // columns of queries past the call's: probability 0 and rescale 1 for good
-  for (int i = threadIdx.x; i < kMqStep * QP; i += kAttnThreads) {
-    const int j = i / QP, q = i % QP;
-    if (q >= nq) s_pt[j][q] = 0.f;
+  // rows of queries past the call's: probability 0 and rescale 1 for good
+  for (int i = threadIdx.x; i < NQT * 2 * 2 * 64 * 8; i += kAttnThreads) {
+    const int l = (i / 8) % 64;
+    const int qt = i / (2 * 2 * 64 * 8);
+    if (16 * qt + (l & 15) >= nq) (&s_pa[0][0][0][0])[i] = 0;
   }
-  for (int q = threadIdx.x; q < QP; q += kAttnThreads)
+  for (int q = threadIdx.x; q < QT; q += kAttnThreads) {
     if (q >= nq) s_sc[q] = 1.f;
-  float m_q[QPW], l_q[QPW], acc[QP];
-#pragma unroll
-  for (int j = 0; j < QPW; ++j) {
-    m_q[j] = -INFINITY;
-    l_q[j] = 0.f;
+    s_m[q] = -INFINITY;
+    s_l[q] = 0.f;
   }
+  // output accumulators: tile qt, dimension tile dt (dimensions
+  // 64 wave + 16 dt ..), lane holds queries 16 qt + 4 (lane / 16) + i of
+  // dimension 64 wave + 16 dt + lane % 16
+  at_f32x4 o_acc[NQT][4];
 #pragma unroll
-  for (int q = 0; q < QP; ++q) acc[q] = 0.f;
+  for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o_acc[qt][dt] = at_f32x4{0.f, 0.f, 0.f, 0.f};
   const int tl = lane & 15, kq = 8 * (lane >> 4);
   // key rows of a step (B operand: position base + 16 wave + tl, dimensions
   // kq + 32 ks .. + 7), requested one step ahead
@@ -382,22 +398,30 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_mq_kernel(AttnArgs a) {
   };
   load_k(c0);
   for (int base = c0; base <= jmax; base += kMqStep) {
-    // this step's values of the lane's dimension, requested first: they
-    // arrive while the scores and the softmax are computed
+    // this step's values as the B operand of the weighted-value product,
+    // requested first (they arrive while the scores and the softmax are
+    // computed): for dimension tile dt and half step kb, lane l holds
+    // dimension 64 wave + 16 dt + l % 16 at positions 32 kb + 8 (l / 16) .. + 7,
+    // two positions per register (16-bit loads into the low and high halves)
     const int jl = min(kMqStep - 1, jmax - base);
-    // (at 64 queries, whose registers would not leave two waves per SIMD
-    // otherwise, half of them now and the other half once the first half
-    // has been used)
-    constexpr int VN = QP >= 48 ? kMqStep / 2 : kMqStep;
-    uint16_t vr[VN];
+    at_u16x2 vb[4][2][4];
 #pragma unroll
-    for (int j = 0; j < VN; ++j) vr[j] = gload<uint16_t>((const uint8_t*)(vcol + (int64_t)(base + min(j, jl)) * D));
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2)
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            const int j = min(32 * h + kq + 2 * e2 + x, jl);
+            vb[dt][h][e2][x] = gload<uint16_t>((const uint8_t*)(vbase + (int64_t)(base + j) * D + 64 * wave + 16 * dt + tl));
+          }
     mq_barrier();  // s_q written (first step); the previous step's LDS reads done
     // (1) scores of positions base + 16 wave + tl for every query tile
     {
-      at_f32x4 sc4[QT / 16];
+      at_f32x4 sc4[NQT];
 #pragma unroll
-      for (int qt = 0; qt < QT / 16; ++qt) {  // every tile: rows past the queries are zeros, masked below
+      for (int qt = 0; qt < NQT; ++qt) {  // every tile: rows past the queries are zeros, masked below
         sc4[qt] = at_f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) {
@@ -408,7 +432,7 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_mq_kernel(AttnArgs a) {
       if (base + kMqStep <= jmax) load_k(base + kMqStep);  // the next step's keys
       const int pos = base + 16 * wave + tl;
 #pragma unroll
-      for (int qt = 0; qt < QT / 16; ++qt) {
+      for (int qt = 0; qt < NQT; ++qt) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int q = 16 * qt + 4 * (lane >> 4) + r;
@@ -418,71 +442,83 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_mq_kernel(AttnArgs a) {
       }
     }
     mq_barrier();
-    // (2) online softmax of queries wave, wave + 4, ... over the step
+    // (2) online softmax of queries wave, wave + 4, ... over the step; the
+    // probability of position `lane` goes to the A operand as hi + lo
 #pragma unroll
     for (int j = 0; j < QPW; ++j) {
       const int q = wave + kAttnWaves * j;
       if (q < nq) {
         const float x = s_s[q][lane];
-        const float mn = fmaxf(m_q[j], wave_max(x));
+        const float m_old = s_m[q];
+        const float mn = fmaxf(m_old, wave_max(x));
         float p = 0.f, sc = 1.f;
         if (mn != -INFINITY) {
           p = x == -INFINITY ? 0.f : expf(x - mn);
-          sc = m_q[j] == -INFINITY ? 0.f : expf(m_q[j] - mn);
+          sc = m_old == -INFINITY ? 0.f : expf(m_old - mn);
         }
         const float sum = wave_sum(p);
-        l_q[j] = l_q[j] * sc + sum;
-        m_q[j] = mn;
-        s_pt[lane][q] = p;
-        if (lane == 0) s_sc[q] = sc;
+        const float l_new = s_l[q] * sc + sum;
+        const uint32_t hi = f32_to_bf16_rne(p);
+        const uint32_t lo = f32_to_bf16_rne(p - __uint_as_float(hi << 16));
+        const int at = (16 * ((lane >> 3) & 3) + (q & 15)) * 8 + (lane & 7);
+        s_pa[q >> 4][lane >> 5][0][at] = (uint16_t)hi;
+        s_pa[q >> 4][lane >> 5][1][at] = (uint16_t)lo;
+        if (lane == 0) {
+          s_sc[q] = sc;
+          s_m[q] = mn;
+          s_l[q] = l_new;
+        }
       }
     }
     mq_barrier();
-    // (3) weighted values: lane owns output dimension 64 wave + lane
+    // (3) weighted values on the matrix cores: rescale, then
+    // o += P_hi V + P_lo V over the step's 64 positions (positions past jl:
+    // p = 0 and a copy of row jl's value)
 #pragma unroll
-    for (int q4 = 0; q4 < QP / 4; ++q4) {  // queries past the call's: rescale 1, probabilities 0
-      const float4 f = *(const float4*)&s_sc[4 * q4];
-      acc[4 * q4] *= f.x;
-      acc[4 * q4 + 1] *= f.y;
-      acc[4 * q4 + 2] *= f.z;
-      acc[4 * q4 + 3] *= f.w;
-    }
-    // positions past jl hold p = 0 for every query and a copy of row jl's value
+    for (int qt = 0; qt < NQT; ++qt) {
+      const float4 f = *(const float4*)&s_sc[16 * qt + 4 * (lane >> 4)];
 #pragma unroll
-    for (int j = 0; j < kMqStep; ++j) {
-      if (VN < kMqStep && j == VN) {
-#pragma unroll
-        for (int i = 0; i < VN; ++i)
-          vr[i] = gload<uint16_t>((const uint8_t*)(vcol + (int64_t)(base + min(VN + i, jl)) * D));
-      }
-      const float v = __uint_as_float((uint32_t)vr[j % VN] << 16);
-      const float* prow = &s_pt[j][0];
-#pragma unroll
-      for (int q4 = 0; q4 < QP / 4; ++q4) {
-        const float4 pq = *(const float4*)&prow[4 * q4];
-        acc[4 * q4] = fmaf(pq.x, v, acc[4 * q4]);
-        acc[4 * q4 + 1] = fmaf(pq.y, v, acc[4 * q4 + 1]);
-        acc[4 * q4 + 2] = fmaf(pq.z, v, acc[4 * q4 + 2]);
-        acc[4 * q4 + 3] = fmaf(pq.w, v, acc[4 * q4 + 3]);
+      for (int dt = 0; dt < 4; ++dt) {
+        o_acc[qt][dt][0] *= f.x;
+        o_acc[qt][dt][1] *= f.y;
+        o_acc[qt][dt][2] *= f.z;
+        o_acc[qt][dt][3] *= f.w;
       }
     }
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x4 ph = *(const u32x4*)&s_pa[qt][h][0][8 * lane];
+        const u32x4 pl = *(const u32x4*)&s_pa[qt][h][1][8 * lane];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const u32x4 vv = __builtin_bit_cast(u32x4, vb[dt][h]);
+          o_acc[qt][dt] = mfma_qk(ph, vv, o_acc[qt][dt]);
+          o_acc[qt][dt] = mfma_qk(pl, vv, o_acc[qt][dt]);
+        }
+      }
   }
   // the chunk's partials of the rows that see it
 #pragma unroll
-  for (int q = 0; q < QP; ++q) {
-    const int t = q / G;
-    if (q < nq && c0 <= a.p0 + t) {
-      float* dst = a.part + (((int64_t)c * a.T + t) * a.n_q + kv * G + q % G) * pstride<D>();
-      dst[4 + 64 * wave + lane] = acc[q];
+  for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = 16 * qt + 4 * (lane >> 4) + i;
+      const int t = q / G;
+      if (q < nq && c0 <= a.p0 + t) {
+        float* dst = a.part + (((int64_t)c * a.T + t) * a.n_q + kv * G + q % G) * pstride<D>();
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) dst[4 + 64 * wave + 16 * dt + tl] = o_acc[qt][dt][i];
+      }
     }
-  }
 #pragma unroll
   for (int j = 0; j < QPW; ++j) {
     const int q = wave + kAttnWaves * j;
     if (q < nq && lane == 0 && c0 <= a.p0 + q / G) {
       float* dst = a.part + (((int64_t)c * a.T + q / G) * a.n_q + kv * G + q % G) * pstride<D>();
-      dst[0] = m_q[j];
-      dst[1] = l_q[j];
+      dst[0] = s_m[q];  // written by this wave (lane 0)
+      dst[1] = s_l[q];
     }
   }
 }
