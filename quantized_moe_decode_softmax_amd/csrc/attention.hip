@@ -405,10 +405,9 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_mq_kernel(AttnArgs a) {
     // two positions per register (16-bit loads into the low and high halves)
     const int jl = min(kMqStep - 1, jmax - base);
     at_u16x2 vb[4][2][4];
+    auto load_v = [&](int h) {
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2)
 #pragma unroll
@@ -416,6 +415,12 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_mq_kernel(AttnArgs a) {
             const int j = min(32 * h + kq + 2 * e2 + x, jl);
             vb[dt][h][e2][x] = gload<uint16_t>((const uint8_t*)(vbase + (int64_t)(base + j) * D + 64 * wave + 16 * dt + tl));
           }
+    };
+    // at four query tiles the second half is requested after the scores,
+    // so that the registers of both halves are not live across them
+    constexpr bool V_SPLIT = NQT >= 4;
+    load_v(0);
+    if constexpr (!V_SPLIT) load_v(1);
     mq_barrier();  // s_q written (first step); the previous step's LDS reads done
     // (1) scores of positions base + 16 wave + tl for every query tile
     {
@@ -430,6 +435,7 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_mq_kernel(AttnArgs a) {
         }
       }
       if (base + kMqStep <= jmax) load_k(base + kMqStep);  // the next step's keys
+      if constexpr (V_SPLIT) load_v(1);
       const int pos = base + 16 * wave + tl;
 #pragma unroll
       for (int qt = 0; qt < NQT; ++qt) {
