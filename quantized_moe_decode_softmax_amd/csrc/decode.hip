@@ -445,7 +445,12 @@ __global__ void __launch_bounds__(1024) select_kernel(Dims d, Ptrs p) {
   for (int t = wave; t < d.T; t += 16) {
     int my_id;
     float my_w, r;
-    wave_topk(p.raw + (int64_t)t * d.E, p.rinv + t, d.E, d.k, my_id, my_w, r);
+    // as many logits per lane as the experts need (lists past E cost work)
+    const float* raw = p.raw + (int64_t)t * d.E;
+    if (d.E <= 64) wave_topk<1>(raw, p.rinv + t, d.E, d.k, my_id, my_w, r);
+    else if (d.E <= 128) wave_topk<2>(raw, p.rinv + t, d.E, d.k, my_id, my_w, r);
+    else if (d.E <= 256) wave_topk<4>(raw, p.rinv + t, d.E, d.k, my_id, my_w, r);
+    else wave_topk<kMaxExperts / 64>(raw, p.rinv + t, d.E, d.k, my_id, my_w, r);
     if (lane < d.k) {  // lane i holds entry i
       const int i = t * d.k + lane;
       p.ids[i] = my_id;

@@ -731,10 +731,11 @@ __device__ __forceinline__ void topk_select(int (&key)[M], int k, int& lane_id, 
 
 // Top-k of one token row on one wave: logits lam_src[0..E) scaled by
 // *scale_src (the RMS factor); lane i < k receives the i-th (id, weight).
+// M: logits per lane, E <= 64 M (the selection does not depend on M).
+template <int M>
 __device__ __forceinline__ void wave_topk(const float* lam_src, const float* scale_src, int E, int k, int& lane_id,
                                           float& lane_w, float& scale_out) {
   const int lane = threadIdx.x & 63;
-  constexpr int M = kMaxExperts / 64;
   const float scale = *scale_src;
   scale_out = scale;
   int key[M];
