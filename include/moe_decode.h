@@ -363,8 +363,10 @@ int32_t moe_generate_matrix(int32_t bits, int32_t rows, int32_t cols, uint64_t s
  * g = n_q / n_kv. The keys are split at fixed multiples of 512 positions, so
  * row i of a T-row call equals a one-row call with p0 + i bit for bit. At
  * head_dim 256 each chunk's K and V are read once for all T x g queries of a
- * KV head (the scores on the matrix cores); at head_dim 64 and 128 once per
- * pass of up to 16 queries (whole verify rows).
+ * KV head (the scores and the weighted values on the matrix cores, the
+ * probabilities entering the latter as two bf16 parts, exact to 2^-18
+ * relative); at head_dim 64 and 128 once per pass of up to 16 queries (whole
+ * verify rows).
  *   shape  : n_q, n_kv with n_q a multiple of n_kv, n_q / n_kv <= 16 (<= 8
  *            at head_dim 256), n_q <= 128; head_dim in {64, 128, 256};
  *            max_seq (cache length)
