@@ -43,9 +43,13 @@ struct GemvArgs {
   const uint16_t* x;        // bf16 [T, K]
 };
 
-template <int BITS, int CPL>
+// DEC (8-bit codes, several token rows): the task's codes are decoded into
+// bf16 pairs once and reused for every token row (the same products and sums
+// as decoding them per row), two rows per task so that the decoded pairs
+// leave four waves per SIMD.
+template <int BITS, int CPL, bool DEC>
 __global__ void __launch_bounds__(64 * kGemvWaves) gemv_kernel(GemvArgs a) {
-  constexpr int R = CPL >= 2 ? 2 : 4;  // rows per row group (registers: R * CPL <= 4)
+  constexpr int R = DEC ? 2 : CPL >= 2 ? 2 : 4;  // rows per row group (registers: R * CPL <= 4)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lpr = lanes_per_row(a.K), rpw = 64 / lpr, sr = lane / lpr, li = lane % lpr;
   const int task = blockIdx.x * kGemvWaves + wave;
@@ -70,9 +74,14 @@ __global__ void __launch_bounds__(64 * kGemvWaves) gemv_kernel(GemvArgs a) {
   load_rows<BITS, CPL, R>(Q, rc, rs, a.K, (int)(a.row_bytes >> 2), li, lpr);
   XLane<BITS, CPL> x;
   float out[R];
+  RowsDec8<CPL, DEC ? R : 1> Dq;
+  if constexpr (DEC) decode8<CPL, R>(Q, Dq);
   for (int t = 0; t < a.T; ++t) {
     prep_x<BITS, CPL>(x, a.x + (int64_t)t * a.K, a.K, li, lpr);
-    dot_rows<BITS, CPL, R, 1>(Q, x, x, out);
+    if constexpr (DEC)
+      dot_dec8<CPL, R>(Dq, x, out);
+    else
+      dot_rows<BITS, CPL, R, 1>(Q, x, x, out);
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const float v = reduce_row(out[i], lpr);
@@ -96,7 +105,14 @@ void launch_gemv(int bits, const GemvArgs& a, hipStream_t st) {
   const int rpw = 64 / lanes_per_row(a.K);
   const int tasks = (a.total + R * rpw - 1) / (R * rpw);
   const int grid = (tasks + kGemvWaves - 1) / kGemvWaves;
-  MOE_GEMV_BITS(bits, B, gemv_kernel<B, CPL><<<grid, 64 * kGemvWaves, 0, st>>>(a));
+  if constexpr (CPL <= 2) {
+    if (bits == 8 && a.T >= 2) {  // codes decoded once for all token rows
+      const int tasks2 = (a.total + 2 * rpw - 1) / (2 * rpw);
+      gemv_kernel<8, CPL, true><<<(tasks2 + kGemvWaves - 1) / kGemvWaves, 64 * kGemvWaves, 0, st>>>(a);
+      return;
+    }
+  }
+  MOE_GEMV_BITS(bits, B, gemv_kernel<B, CPL, false><<<grid, 64 * kGemvWaves, 0, st>>>(a));
 }
 
 }  // namespace

@@ -539,6 +539,57 @@ __device__ __forceinline__ void dot_rows(RowsQ<BITS, CPL, R>& Q, const XLane<BIT
   }
 }
 
+// 8-bit rows decoded once for several token rows: the bf16 pairs that
+// byte_dots builds from each code dword (nibble planes at shifts 0, 8 for the
+// low plane, 4, 12 for the high one), kept in registers, and the scale/bias
+// word. dot_dec8 then adds, for one token row, exactly the products and sums
+// of dot_rows<8, CPL, R, 1> in the same order, so results are bit for bit
+// those of the fused decode.
+template <int CPL, int R>
+struct RowsDec8 {
+  uint32_t p[R][CPL][32];
+  uint32_t sb[R][CPL];
+};
+template <int CPL, int R>
+__device__ __forceinline__ void decode8(const RowsQ<8, CPL, R>& Q, RowsDec8<CPL, R>& D) {
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t q = Q.q[r][c][k];
+        D.p[r][c][4 * k + 0] = (q & kM4) | kMagic;
+        D.p[r][c][4 * k + 1] = ((q >> 8) & kM4) | kMagic;
+        D.p[r][c][4 * k + 2] = ((q >> 4) & kM4) | kMagic;
+        D.p[r][c][4 * k + 3] = ((q >> 12) & kM4) | kMagic;
+      }
+      D.sb[r][c] = Q.sb[r][c];
+    }
+}
+template <int CPL, int R>
+__device__ __forceinline__ void dot_dec8(const RowsDec8<CPL, R>& D, const XLane<8, CPL>& x, float (&out)[R]) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      float dl = 0.f, dh = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        dot2c(dl, D.p[r][c][4 * k + 0], x.w[c][2 * k]);
+        dot2c(dl, D.p[r][c][4 * k + 1], x.w[c][2 * k + 1]);
+        dot2c(dh, D.p[r][c][4 * k + 2], x.w[c][2 * k]);
+        dot2c(dh, D.p[r][c][4 * k + 3], x.w[c][2 * k + 1]);
+      }
+      dot_fence(dl, dh);
+      const float s = bf16_lo_to_f32(D.sb[r][c]), b = bf16_hi_to_f32(D.sb[r][c]);
+      acc += fmaf(s, fmaf(16.f, dh, dl), (b - 2176.f * s) * x.s[c]);
+    }
+    out[r] = acc;
+  }
+}
+
 // Dense bf16 rows (a bf16 router): 16 words per chunk.
 template <int CPL, int R>
 struct RowsD {
