@@ -360,8 +360,11 @@ int32_t moe_generate_matrix(int32_t bits, int32_t rows, int32_t cols, uint64_t s
  * checkpoint": 16 query heads, 2 KV heads, head dimension 256). Row i is at
  * position p0 + i and attends to positions 0 .. p0 + i:
  *   o[i, h] = sum_j softmax_j(q[i, h] . K[h / g, j] / sqrt(d)) V[h / g, j],
- * g = n_q / n_kv. The keys are split at fixed multiples of 512 positions, so
- * row i of a T-row call equals a one-row call with p0 + i bit for bit. At
+ * g = n_q / n_kv. The keys are split at fixed multiples of a chunk that
+ * depends on the cache alone (head_dim 64 and 128: 512 positions; head_dim
+ * 256: the largest of 512, 256, 128 and 64 positions that gives at least 512
+ * chunks x KV heads over max_seq, else 64), so row i of a T-row call equals a
+ * one-row call with p0 + i on the same cache bit for bit. At
  * head_dim 256 each chunk's K and V are read once for all T x g queries of a
  * KV head (the scores and the weighted values on the matrix cores, the
  * probabilities entering the latter as two bf16 parts, exact to 2^-18

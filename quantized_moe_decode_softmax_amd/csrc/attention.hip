@@ -2,7 +2,7 @@
 // i = 0..T-1 at positions p0 + i attend causally to the cache, query head h
 // to KV head h / g. moe_gqa_decode computes it in two kernels:
 //
-//   partial kernel       one workgroup per (chunk of kChunk positions, KV head)
+//   partial kernel       one workgroup per (chunk of positions, KV head)
 //                        keeps, per (row, head), the running maximum, the sum
 //                        of exponentials and the weighted sum of values
 //                        (online softmax) and stores (max, sum, acc[d]) for
@@ -17,7 +17,8 @@
 //                        row sees in a grouping fixed by their number, and
 //                        divides.
 //
-// Split points are the fixed multiples of kChunk, and every sum runs in an
+// Split points are the fixed multiples of the chunk (chunk_of: from the
+// cache's capacity and KV heads alone), and every sum runs in an
 // order fixed by the position alone, so a row of a T-row call equals a one-row
 // call at that position bit for bit (PureDrive-35B-A3B-MLX model card, "How it
 // works": K/V read once for all query heads of a KV head and all verify rows,
@@ -46,6 +47,7 @@ constexpr int kMaxHeadDim = 256;
 
 struct AttnArgs {
   int n_q, n_kv, g, S, T, p0, n_chunks, rg;    // rg: verify rows per pass (rg * g <= queries per pass)
+  int chunk;                                   // positions per workgroup (chunk_of)
   float scale;                                 // 1 / sqrt(d)
   const uint16_t* q;                           // bf16 [T][n_q][D]
   const uint16_t* k;                           // bf16 [n_kv][S][D]
@@ -357,8 +359,8 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_mq_kernel(AttnArgs a) {
   __shared__ float s_m[QT], s_l[QT];                                   // running maximum and sum of each query
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = blockIdx.x, kv = blockIdx.y;
-  const int c0 = c * kChunk;
-  const int jmax = min(c0 + kChunk - 1, a.p0 + a.T - 1);  // last position any row sees
+  const int c0 = c * a.chunk;
+  const int jmax = min(c0 + a.chunk - 1, a.p0 + a.T - 1);  // last position any row sees
   if (c0 > jmax) return;
   const int nq = a.T * G, nqt = (nq + 15) / 16;
   const uint16_t* kbase = a.k + (int64_t)kv * a.S * D;
@@ -545,7 +547,7 @@ __global__ void __launch_bounds__(64 * kCombWaves) attn_combine_kernel(AttnArgs 
   __shared__ float s_o[kCombWaves][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x / a.n_q, h = blockIdx.x % a.n_q, e = blockIdx.y * 64 + lane;
-  const int nc = (a.p0 + t) / kChunk + 1;
+  const int nc = (a.p0 + t) / a.chunk + 1;
   const float* base = a.part + ((int64_t)t * a.n_q + h) * pstride<D>();
   const int64_t cs = (int64_t)a.T * a.n_q * pstride<D>();  // chunk stride
   float mw = -INFINITY, L = 0.f, o = 0.f;
@@ -596,8 +598,22 @@ __global__ void __launch_bounds__(64 * kCombWaves) attn_combine_kernel(AttnArgs 
   }
 }
 
-int64_t attn_ws_bytes(int n_q, int D, int T, int max_seq) {
-  const int64_t n_chunks = (max_seq + kChunk - 1) / kChunk;
+// Positions per workgroup. Head dimension 256: the largest of 512, 256, 128
+// and 64 that still gives 512 workgroups (two per compute unit) over a full
+// cache, else 64, so that short caches are not a few workgroups of many
+// dependent steps; it depends on the cache's capacity and KV heads alone, so
+// every call on one cache splits at the same points. Head dimensions 64 and
+// 128: kChunk (the kernel's two passes of kSub positions).
+int chunk_of(int D, int max_seq, int n_kv) {
+  if (D != 256) return kChunk;
+  for (int c = kChunk; c > kMqStep; c /= 2)
+    if ((int64_t)((max_seq + c - 1) / c) * n_kv >= 512) return c;
+  return kMqStep;
+}
+
+int64_t attn_ws_bytes(int n_q, int n_kv, int D, int T, int max_seq) {
+  const int chunk = chunk_of(D, max_seq, n_kv);
+  const int64_t n_chunks = (max_seq + chunk - 1) / chunk;
   return align_up(n_chunks * T * n_q * (int64_t)(D + 4) * 4, kAlign);
 }
 
@@ -627,7 +643,7 @@ extern "C" int64_t moe_gqa_workspace_bytes(const moe_attn_shape_t* shape, int32_
   clear_error();
   int32_t rc = check_attn(shape, T);
   if (rc) return rc;
-  return attn_ws_bytes(shape->n_q, shape->head_dim, T, shape->max_seq);
+  return attn_ws_bytes(shape->n_q, shape->n_kv, shape->head_dim, T, shape->max_seq);
 }
 
 extern "C" int32_t moe_gqa_decode(const moe_attn_shape_t* shape, int32_t T, int32_t p0, const uint16_t* q_dev,
@@ -643,7 +659,7 @@ extern "C" int32_t moe_gqa_decode(const moe_attn_shape_t* shape, int32_t T, int3
   if ((uintptr_t)q_dev % 16 || (uintptr_t)k_dev % 16 || (uintptr_t)v_dev % 16 || (uintptr_t)o_dev % 16)
     return set_error(MOE_ERR_ALIGNMENT, "q, k, v and o must be 16-byte aligned");
   if ((uintptr_t)ws_dev % kAlign) return set_error(MOE_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
-  const int64_t need = attn_ws_bytes(s.n_q, s.head_dim, T, s.max_seq);
+  const int64_t need = attn_ws_bytes(s.n_q, s.n_kv, s.head_dim, T, s.max_seq);
   if ((int64_t)ws_bytes < need)
     return set_error(MOE_ERR_WORKSPACE, "workspace %zu bytes < %lld needed", ws_bytes, (long long)need);
   AttnArgs a;
@@ -653,7 +669,8 @@ extern "C" int32_t moe_gqa_decode(const moe_attn_shape_t* shape, int32_t T, int3
   a.S = s.max_seq;
   a.T = T;
   a.p0 = p0;
-  a.n_chunks = (p0 + T - 1) / kChunk + 1;
+  a.chunk = chunk_of(s.head_dim, s.max_seq, s.n_kv);
+  a.n_chunks = (p0 + T - 1) / a.chunk + 1;
   a.rg = qg_of_dim(s.head_dim) / a.g;  // (rows per pass; the kernels take it from their G)
   a.scale = (float)(1.0 / std::sqrt((double)s.head_dim));
   a.q = q_dev;

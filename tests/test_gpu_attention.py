@@ -9,8 +9,10 @@
 * cache positions past the last row hold NaN and are never read (the output
   stays finite and equal);
 * position 0 alone returns v_0 exactly;
-* the card's shape (16 query heads, 2 KV heads, head dim 256) over a cache of
-  40,000 positions, T = 1 and 3 near the end, all heads against the oracle.
+* the card's shape (16 query heads, 2 KV heads, head dim 256) over caches of
+  40,000 and 131,072 positions (chunks of 128 and 512 positions; the small
+  caches above use 64), T = 1 and 3 near the end, all heads against the
+  oracle.
 """
 
 import sys
@@ -109,9 +111,10 @@ def test_attention_unfilled_positions_not_read_and_single_key():
         assert torch.equal(o0[0, h], v0[h // 8])
 
 
-def test_attention_card_shape_long_cache():
-    c = Cache(16, 2, 256, 40000, seed=5)
-    for T, p0 in ((1, 39998), (3, 39990)):
+@pytest.mark.parametrize("S", [40000, 131072], ids=["chunk128", "chunk512"])
+def test_attention_card_shape_long_cache(S):
+    c = Cache(16, 2, 256, S, seed=5)
+    for T, p0 in ((1, S - 2), (3, S - 10)):
         q = c.q(900 + T, T)
         o = c.run(q, p0)
         torch.cuda.synchronize()

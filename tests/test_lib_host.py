@@ -380,7 +380,15 @@ def test_gqa_argument_errors():
     A = 1 << 20
     ok = moe.moe_attn_shape_t(16, 2, 256, 4096)
     ws = moe.moe_gqa_workspace_bytes(ok, 3)
-    assert ws == ((4096 + 511) // 512) * 3 * 16 * (256 + 4) * 4
+    # head dim 256: chunks of 64 positions here (4096 / 512 x 2 KV heads < 512
+    # chunks for every larger size), one partial (max, sum, pad, acc[d]) each
+    assert ws == (4096 // 64) * 3 * 16 * (256 + 4) * 4
+    # the card's cache of 131,072 positions: chunks of 512 (256 x 2 KV heads)
+    assert moe.moe_gqa_workspace_bytes(moe.moe_attn_shape_t(16, 2, 256, 131072), 1) == 256 * 16 * 260 * 4
+    # 40,000 positions: 128 (313 chunks x 2 >= 512; 157 x 2 at 256 is not)
+    assert moe.moe_gqa_workspace_bytes(moe.moe_attn_shape_t(16, 2, 256, 40000), 1) == 313 * 16 * 260 * 4
+    # head dims 64 and 128 keep 512 (two passes of 256 positions)
+    assert moe.moe_gqa_workspace_bytes(moe.moe_attn_shape_t(16, 2, 128, 4096), 2) == 8 * 2 * 16 * 132 * 4
     for sh, code in [(moe.moe_attn_shape_t(16, 2, 96, 4096), moe.MOE_ERR_UNSUPPORTED),
                      (moe.moe_attn_shape_t(15, 2, 256, 4096), moe.MOE_ERR_UNSUPPORTED),
                      (moe.moe_attn_shape_t(32, 2, 256, 4096), moe.MOE_ERR_UNSUPPORTED),  # 16 per KV head at d 256
