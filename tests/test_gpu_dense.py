@@ -75,6 +75,7 @@ CASES = [
     (3, 1024, (40,)),
     (2, 8192, (17, 9)),
     (8, 8192, (21,)),
+    (8, 4096, (19, 66)),  # two chunks per lane: the decoded-once path at T >= 2
 ]
 
 
